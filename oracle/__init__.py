@@ -1,0 +1,247 @@
+"""CPU oracle for the block-scaled quantizers -- TEST INFRASTRUCTURE ONLY.
+
+The C file ``mxq_oracle.c`` beside this module is the plain single-threaded
+definition of every output byte (MXFP8 row-/column-wise with pad-then-crop,
+dequantization and fake-quant, grouped row-wise, 128x128 block-FP8, NVFP4).
+This module only marshals numpy arrays into it through ctypes.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this package.  The HIP product path never imports it and the
+two share no code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxq_oracle.c")
+_LIB = os.path.join(_HERE, "libmxq_oracle.so")
+
+# Strict IEEE: no contraction into FMA, no fast-math, SSE arithmetic (x86-64
+# default, FLT_EVAL_METHOD == 0), no flush-to-zero.
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+          "-fexcess-precision=standard", "-Wall", "-Wextra", "-shared", "-fPIC"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libmxq_oracle.so``."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_i64 = ctypes.c_int64
+
+
+def _p(a: np.ndarray, ct):
+    assert a.flags["C_CONTIGUOUS"], "oracle buffers must be C-contiguous"
+    return a.ctypes.data_as(ct)
+
+
+def _bits16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    assert x.dtype == np.uint16 and x.ndim == 2, "bf16 inputs are passed as uint16 [rows, cols]"
+    return x
+
+
+class Oracle:
+    """numpy-facing wrapper over one build of the oracle library.
+
+    The tests also build deliberately broken copies of the C source and wrap
+    them in this class, to show that the pins catch planted mistakes."""
+
+    def __init__(self, path: str):
+        L = ctypes.CDLL(path)
+        L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_double.restype = ctypes.c_double
+        L.orc_double_to_bf16.argtypes = [ctypes.c_double]
+        L.orc_double_to_bf16.restype = ctypes.c_uint16
+        L.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_to_double.restype = ctypes.c_double
+        L.orc_double_to_e4m3.argtypes = [ctypes.c_double]
+        L.orc_double_to_e4m3.restype = ctypes.c_uint8
+        L.orc_e8m0_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_to_double.restype = ctypes.c_double
+        L.orc_e2m1_to_double.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_to_double.restype = ctypes.c_double
+        L.orc_double_to_e2m1.argtypes = [ctypes.c_double]
+        L.orc_double_to_e2m1.restype = ctypes.c_uint8
+        L.orc_mxfp8_quantize_rowwise.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
+        L.orc_mxfp8_quantize_rowwise.restype = None
+        L.orc_mxfp8_quantize_padcrop.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
+        L.orc_mxfp8_quantize_padcrop.restype = ctypes.c_int
+        L.orc_mxfp8_quantize_colwise.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
+        L.orc_mxfp8_quantize_colwise.restype = None
+        L.orc_mxfp8_dequantize.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_int, _u16p]
+        L.orc_mxfp8_dequantize.restype = None
+        L.orc_mxfp8_fake_quant.argtypes = [_u16p, _i64, _i64, ctypes.c_int, _u16p]
+        L.orc_mxfp8_fake_quant.restype = ctypes.c_int
+        L.orc_blockfp8_quantize.argtypes = [_u16p, _i64, _i64, ctypes.c_int32, _u8p, _f32p]
+        L.orc_blockfp8_quantize.restype = None
+        L.orc_blockfp8_dequantize.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int32, _u16p]
+        L.orc_blockfp8_dequantize.restype = None
+        L.orc_nvfp4_quantize.argtypes = [_u16p, _i64, _i64, _u8p, _u8p, _f32p]
+        L.orc_nvfp4_quantize.restype = None
+        L.orc_nvfp4_dequantize.argtypes = [_u8p, _u8p, _f32p, _i64, _i64, _u16p]
+        L.orc_nvfp4_dequantize.restype = None
+        self.L = L
+        self.path = path
+
+    # ---- scalar codecs ----------------------------------------------------
+    def bf16_to_double(self, b: int) -> float:
+        return self.L.orc_bf16_to_double(int(b))
+
+    def double_to_bf16(self, v: float) -> int:
+        return self.L.orc_double_to_bf16(float(v))
+
+    def e4m3_to_double(self, c: int) -> float:
+        return self.L.orc_e4m3_to_double(int(c))
+
+    def double_to_e4m3(self, v: float) -> int:
+        return self.L.orc_double_to_e4m3(float(v))
+
+    def e8m0_to_double(self, b: int) -> float:
+        return self.L.orc_e8m0_to_double(int(b))
+
+    def e2m1_to_double(self, n: int) -> float:
+        return self.L.orc_e2m1_to_double(int(n))
+
+    def double_to_e2m1(self, v: float) -> int:
+        return self.L.orc_double_to_e2m1(float(v))
+
+    # ---- MXFP8 ------------------------------------------------------------
+    def mxfp8_quantize_rowwise(self, x: np.ndarray):
+        """x: uint16 bf16 bits [rows, cols], cols % 32 == 0 ->
+        (q [rows, cols] u8, scale [rows, cols/32] u8)."""
+        x = _bits16(x)
+        rows, cols = x.shape
+        assert cols % 32 == 0
+        q = np.empty((rows, cols), np.uint8)
+        s = np.empty((rows, cols // 32), np.uint8)
+        self.L.orc_mxfp8_quantize_rowwise(_p(x, _u16p), rows, cols, _p(q, _u8p), _p(s, _u8p))
+        return q, s
+
+    def mxfp8_quantize_padcrop(self, x: np.ndarray):
+        x = _bits16(x)
+        rows, cols = x.shape
+        assert cols % 32 == 0
+        q = np.empty((rows, cols), np.uint8)
+        s = np.empty((rows, cols // 32), np.uint8)
+        rc = self.L.orc_mxfp8_quantize_padcrop(_p(x, _u16p), rows, cols, _p(q, _u8p), _p(s, _u8p))
+        assert rc == 0
+        return q, s
+
+    def mxfp8_quantize_colwise(self, x: np.ndarray):
+        """-> (q [rows, cols] u8 in x's layout, scale [ceil(rows/32), cols] u8)."""
+        x = _bits16(x)
+        rows, cols = x.shape
+        q = np.empty((rows, cols), np.uint8)
+        s = np.empty(((rows + 31) // 32, cols), np.uint8)
+        self.L.orc_mxfp8_quantize_colwise(_p(x, _u16p), rows, cols, _p(q, _u8p), _p(s, _u8p))
+        return q, s
+
+    def mxfp8_dequantize(self, q: np.ndarray, scale: np.ndarray, axis: int = 1) -> np.ndarray:
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        scale = np.ascontiguousarray(scale, dtype=np.uint8)
+        rows, cols = q.shape
+        out = np.empty((rows, cols), np.uint16)
+        self.L.orc_mxfp8_dequantize(_p(q, _u8p), _p(scale, _u8p), rows, cols, int(axis),
+                                    _p(out, _u16p))
+        return out
+
+    def mxfp8_fake_quant(self, x: np.ndarray, axis: int = 1) -> np.ndarray:
+        x = _bits16(x)
+        rows, cols = x.shape
+        out = np.empty((rows, cols), np.uint16)
+        rc = self.L.orc_mxfp8_fake_quant(_p(x, _u16p), rows, cols, int(axis), _p(out, _u16p))
+        assert rc == 0
+        return out
+
+    def mxfp8_quantize_rowwise_many(self, xs):
+        """Independent row-wise quantization of each tensor, in order."""
+        return [self.mxfp8_quantize_rowwise(x) for x in xs]
+
+    # ---- block-FP8 --------------------------------------------------------
+    def blockfp8_quantize(self, x: np.ndarray, blk: int = 128):
+        x = _bits16(x)
+        rows, cols = x.shape
+        q = np.empty((rows, cols), np.uint8)
+        S = np.empty(((rows + blk - 1) // blk, (cols + blk - 1) // blk), np.float32)
+        self.L.orc_blockfp8_quantize(_p(x, _u16p), rows, cols, int(blk), _p(q, _u8p), _p(S, _f32p))
+        return q, S
+
+    def blockfp8_dequantize(self, q: np.ndarray, S: np.ndarray, blk: int = 128) -> np.ndarray:
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        S = np.ascontiguousarray(S, dtype=np.float32)
+        rows, cols = q.shape
+        out = np.empty((rows, cols), np.uint16)
+        self.L.orc_blockfp8_dequantize(_p(q, _u8p), _p(S, _f32p), rows, cols, int(blk),
+                                       _p(out, _u16p))
+        return out
+
+    # ---- NVFP4 ------------------------------------------------------------
+    def nvfp4_quantize(self, x: np.ndarray):
+        """-> (q_packed [rows, cols/2] u8, s [rows, cols/16] u8 E4M3, g float32 [1])."""
+        x = _bits16(x)
+        rows, cols = x.shape
+        assert cols % 16 == 0
+        q = np.empty((rows, cols // 2), np.uint8)
+        s = np.empty((rows, cols // 16), np.uint8)
+        g = np.empty((1,), np.float32)
+        self.L.orc_nvfp4_quantize(_p(x, _u16p), rows, cols, _p(q, _u8p), _p(s, _u8p), _p(g, _f32p))
+        return q, s, g
+
+    def nvfp4_dequantize(self, q: np.ndarray, s: np.ndarray, g: np.ndarray) -> np.ndarray:
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s = np.ascontiguousarray(s, dtype=np.uint8)
+        g = np.ascontiguousarray(g, dtype=np.float32).reshape(1)
+        rows, half = q.shape
+        cols = half * 2
+        out = np.empty((rows, cols), np.uint16)
+        self.L.orc_nvfp4_dequantize(_p(q, _u8p), _p(s, _u8p), _p(g, _f32p), rows, cols,
+                                    _p(out, _u16p))
+        return out
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``mxq_oracle.c`` (compiled on first use if needed)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _default = Oracle(_LIB)
+    return _default
+
+
+def build_variant(source_text: str, out_path: str) -> Oracle:
+    """Compile an edited copy of the oracle source (used only by the tests that
+    plant mistakes to check the pins) and wrap it."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(source_text)
+    subprocess.run(["gcc", *CFLAGS, src, "-o", out_path, "-lm"], check=True)
+    return Oracle(out_path)
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def __getattr__(name):
+    # Module-level shortcuts: oracle.mxfp8_quantize_rowwise(x) etc.
+    if not name.startswith("_") and hasattr(Oracle, name):
+        return getattr(default(), name)
+    raise AttributeError(name)

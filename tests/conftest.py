@@ -1,0 +1,44 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: CPU test that takes more than ~20 s")
+
+
+def read_golden(name):
+    """Rows of a whitespace-separated golden fixture, comments stripped."""
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    return oracle.default()
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """The HIP library on cuda:0.  Skips only when no GPU is visible; a GPU machine
+    without the built library fails loudly."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible (run with -m gpu on an MI355X)")
+    import block_scaled_precision_mxfp8_amd as mxq
+    mxq.load()  # raises if libmxq.so is missing or stale
+    return mxq

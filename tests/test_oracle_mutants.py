@@ -1,0 +1,80 @@
+"""Plant one mistake at a time in a copy of the oracle's C source (on the CPU)
+and check that the pins catch it: each mutant must fail at least one pin."""
+import numpy as np
+import pytest
+
+import oracle
+import pins
+import workloads
+
+# (name, exact text in the oracle source, replacement)
+MUTANTS = [
+    ("scale exponent off by one", "floor_log2(amax) - 8;", "floor_log2(amax) - 7;"),
+    ("scale clamp at 2^-126", "if (E < -127) E = -127;", "if (E < -126) E = -126;"),
+    ("zero group scale 1.0", "if (amax == 0.0) return 0;", "if (amax == 0.0) return 127;"),
+    ("Inf not a NaN group", "if (!isfinite(a)) return 0xFF;", "if (isnan(a)) return 0xFF;"),
+    ("E4M3 ties away from zero",
+     "double quantum = ldexp(1.0, E - 3);     /* 3 fraction bits */\n    double n = nearbyint(a / quantum);",
+     "double quantum = ldexp(1.0, E - 3);     /* 3 fraction bits */\n    double n = round(a / quantum);"),
+    ("E4M3 subnormal quantum", "if (E < -6) E = -6; ", "if (E < -7) E = -7; "),
+    ("E4M3 no saturation below 480", "if (r > 448.0) return sign | 0x7E;", "if (r > 480.0) return sign | 0x7E;"),
+    ("E4M3 drops sign of small codes", "if (r < ldexp(1.0, -6)) return sign | (uint8_t)n;",
+     "if (r < ldexp(1.0, -6)) return (uint8_t)n;"),
+    ("bf16 rounding flushes subnormals", "if (E < -126) E = -126;", "if (E < -126) return sign;"),
+    ("dequant scale index", "scale[r * (cols / MX_GROUP) + c / MX_GROUP]",
+     "scale[r * (cols / MX_GROUP) + (c % (cols / MX_GROUP))]"),
+    ("colwise scale transposed", "scale[j * cols + c] = s;", "scale[c * nrg + j] = s;"),
+    ("colwise group stride", "q[(r0 + i) * cols + c] = mx_encode(g[i], s);",
+     "q[(r0 + i) * cols + c] = mx_encode(g[i], (uint8_t)(s + (i == 31)));"),
+    ("blockfp8 divisor 447", "S = (float)amax / 448.0f;", "S = (float)amax / 447.0f;"),
+    ("blockfp8 zero tile unguarded", "divisor = (amax == 0.0) ? 1.0f : S;", "divisor = S;"),
+    ("blockfp8 reciprocal multiply", "float t = xf / divisor;", "float t = xf * (1.0f / divisor);"),
+    ("nvfp4 global 2687", "float g = (float)A / 2688.0f;", "float g = (float)A / 2687.0f;"),
+    ("nvfp4 nibble order", "(uint8_t)(nib[i] | (nib[i + 1] << 4));", "(uint8_t)(nib[i + 1] | (nib[i] << 4));"),
+    ("nvfp4 eff divides", "float eff = (float)orc_e4m3_to_double(s) * g;",
+     "float eff = (float)orc_e4m3_to_double(s) / g;"),
+    ("nvfp4 block scale without 6", "float d = 6.0f * g;", "float d = 4.0f * g;"),
+    ("e2m1 saturates at 4", "if (r > 6.0) return sign | 0x7;", "if (r > 4.0) return sign | 0x6;"),
+    ("e2m1 quantum", "if (E < 0) E = 0; ", "if (E < -1) E = -1; "),
+    ("dequant NaN sign", "o = (uint16_t)((code & 0x80) ? 0xFFC0 : 0x7FC0);", "o = (uint16_t)0x7FC0;"),
+]
+
+
+def all_pins(orc):
+    """Every pin, at sizes that keep one pass to a few seconds."""
+    pins.pin_bf16_decode(orc)
+    pins.pin_e4m3_decode(orc)
+    pins.pin_e8m0_decode(orc)
+    pins.pin_e2m1_decode(orc)
+    pins.pin_e4m3_encode_golden(orc)
+    pins.pin_e4m3_encode_bruteforce(orc)
+    pins.pin_e2m1_encode(orc)
+    pins.pin_bf16_round(orc, n_random=20_000)
+    pins.pin_mx_sweep(orc, scale_bytes=list(range(0, 24)) + list(range(24, 247, 11)))
+    pins.pin_mx_nonfinite(orc)
+    pins.pin_mx_edge_groups(orc)
+    x = workloads.random_bf16((97, 256), 17)
+    pins.pin_mx_max_code_band(orc, x)
+    pins.pin_mx_padcrop(orc, x)
+    pins.pin_mx_colwise_is_rowwise_of_transpose(orc, workloads.random_bf16((70, 96), 18))
+    pins.pin_mx_dequant_vs_torch(orc)
+    pins.pin_mx_roundtrip(orc, workloads.mx_small())
+    pins.pin_blockfp8(orc, workloads.random_bf16((200, 300), 19), 128)
+    z = workloads.random_bf16((128, 256), 20)
+    z[:, :128] = 0
+    pins.pin_blockfp8(orc, z, 128)
+    pins.pin_nvfp4(orc, workloads.random_bf16((64, 256), 21))
+
+
+def test_unmutated_source_passes_all_pins(tmp_path):
+    all_pins(oracle.build_variant(oracle.source_text(), str(tmp_path / "orc_same.so")))
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) == 1, f"mutation site not unique/found: {old!r}"
+    orc = oracle.build_variant(src.replace(old, new), str(tmp_path / "orc_mut.so"))
+    with pytest.raises(AssertionError):
+        with np.errstate(all="ignore"):
+            all_pins(orc)
