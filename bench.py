@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Throughput of the MXFP8 quantizer on one MI355X.
+
+One step = one pass of the hot path over the [16384, 7168] bf16 activation
+(0.5 * Student-t(3), seeded): MXFP8 column-wise (groups of 32 tokens),
+row-wise (groups of 32 along hidden) and the fused row-wise fake-quant, all
+from a single read of the input.  ``value`` is algorithmic bytes (bf16 in +
+codes, scales and fake-quant out) per second over the timed steps, inputs
+resident in HBM.  Prints one JSON line.
+
+Besides the timed steps it reports, in the same line:
+  roofline      the one-pass kernel's achieved GB/s (HIP events on the stream
+                it runs on) against MI355X's 8 TB/s HBM peak, plus HBM traffic
+                from the committed rocprofv3 counter summary when it still
+                matches the kernel source
+  cpu_baseline  the CPU oracle (single-threaded C) timed on a bounded sample
+                of the same workload
+  breakdown     every other quantizer workload (row-wise weight, grouped MoE
+                experts, block-FP8, NVFP4, dequantizers), each timed on its own
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "MXFP8 quantize GB/s (bf16 in + fp8/scale out) and % of HBM peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_mxfp8_amd", "csrc", f)
+                  for f in ("mx_kernels.hip", "mxq_device.hpp")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = kernel_source_hash()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 3 and parts[0] == "traffic" and parts[1] == workload:
+                kv = dict(p.split("=", 1) for p in parts[2:] if "=" in p)
+                if kv.get("source") != src:
+                    return None
+                return float(kv["bytes"])
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="rows of the activation the CPU oracle baseline processes")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this quantizer has no cross-GPU step "
+              f"(--gpus {args.gpus}, WORLD_SIZE {world} requested); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_mxfp8_amd as mxq
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+    lib = mxq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def P(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {mxq.status_string(st)}")
+
+    # ------------------------------------------------------------------
+    # main workload: one-pass column-wise + row-wise + fake-quant
+    # ------------------------------------------------------------------
+    rows, cols = workloads.SHAPES["act_16384"]
+    log(f"generating act_16384 [{rows}, {cols}]")
+    xb = workloads.act_16384()
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    e = rows * cols
+    qc = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    sc = torch.empty(((rows + 31) // 32, cols), dtype=torch.uint8, device=dev)
+    qr = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    sr = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    fq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    step_bytes = 2 * e + e + e // 32 + e + sc.numel() + 2 * e
+
+    def step():
+        check(lib.mxq_quantize_colwise(P(x), rows, cols, P(qc), P(sc), P(qr), P(sr), P(fq), sp),
+              "mxq_quantize_colwise")
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # per-launch durations of the kernel (one launch per step), HIP events
+    durs = []
+    for _ in range(max(10, min(args.steps, 50))):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        durs.append(a.elapsed_time(b))
+    kern_ms = statistics.mean(durs)
+    achieved = step_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = read_traffic("act_16384")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "mx_colwise_kernel<col,row,fq>", "algorithmic_bytes": step_bytes,
+                "avg_launch_us": round(kern_ms * 1e3, 2)}
+    log(f"main: {value:.1f} GB/s per step, kernel {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
+
+    # plain device copy of the same byte count: the practical ceiling
+    half = step_bytes // 2
+    src = torch.empty(half, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    cdur = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        b.synchronize()
+        cdur.append(a.elapsed_time(b))
+    copy_gbs = 2 * half / (statistics.median(cdur) * 1e-3) / 1e9
+    del src, dst
+
+    # ------------------------------------------------------------------
+    # CPU oracle on a bounded sample (first cpu_rows rows, same arithmetic)
+    # ------------------------------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        sample = np.ascontiguousarray(xb[:args.cpu_rows])
+        se = sample.size
+        log(f"cpu oracle on [{args.cpu_rows}, {cols}]")
+        t = time.perf_counter()
+        oq, os_ = orc.mxfp8_quantize_rowwise(sample)
+        orc.mxfp8_quantize_colwise(sample)
+        orc.mxfp8_dequantize(oq, os_, 1)
+        dt = time.perf_counter() - t
+        sbytes = 2 * se + se + se // 32 + se + ((args.cpu_rows + 31) // 32) * cols + 2 * se
+        cpu = {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {args.cpu_rows} of {rows} rows of the same input: row-wise + "
+                         f"column-wise quantize and row-wise dequantize, {dt:.1f} s single-threaded"}
+
+    # ------------------------------------------------------------------
+    # breakdown: every other workload, timed on its own
+    # ------------------------------------------------------------------
+    breakdown = {}
+    if not args.no_breakdown:
+        flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+
+        def timed(fn, nbytes, iters=20, flush_cache=True):
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(iters):
+                if flush_cache:
+                    flush.zero_()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                b.synchronize()
+                ts.append(a.elapsed_time(b))
+            ms = statistics.median(ts)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            return {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(nbytes)}
+
+        # the main tensor, one output family at a time
+        breakdown["act_16384 row-wise only"] = timed(
+            lambda: check(lib.mxq_quantize_rowwise(P(x), rows, cols, cols, P(qr), cols, P(sr),
+                                                   cols // 32, None, 0, sp), "rowwise"),
+            2 * e + e + e // 32, flush_cache=False)
+        breakdown["act_16384 column-wise only"] = timed(
+            lambda: check(lib.mxq_quantize_colwise(P(x), rows, cols, P(qc), P(sc), None, None,
+                                                   None, sp), "colwise"),
+            2 * e + e + sc.numel(), flush_cache=False)
+        breakdown["act_16384 fake-quant only"] = timed(
+            lambda: check(lib.mxq_fake_quant(P(x), rows, cols, 1, P(fq), sp), "fake_quant"),
+            4 * e, flush_cache=False)
+        del qc, sc, fq
+
+        # weight [4097, 7168] row-wise (pad-then-crop case)
+        wb = workloads.weight_4097()
+        w = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(dev)
+        wr, wc = wb.shape
+        wq = torch.empty((wr, wc), dtype=torch.uint8, device=dev)
+        ws = torch.empty((wr, wc // 32), dtype=torch.uint8, device=dev)
+        breakdown["weight_4097 row-wise"] = timed(
+            lambda: check(lib.mxq_quantize_rowwise(P(w), wr, wc, wc, P(wq), wc, P(ws), wc // 32,
+                                                   None, 0, sp), "rowwise"),
+            3 * wr * wc + wr * wc // 32)
+        del w, wq, ws
+
+        # mx_small row-wise + dequantize
+        mb = workloads.mx_small()
+        m = torch.from_numpy(mb.view(np.int16)).view(torch.bfloat16).to(dev)
+        mq = torch.empty(mb.shape, dtype=torch.uint8, device=dev)
+        ms_ = torch.empty((mb.shape[0], mb.shape[1] // 32), dtype=torch.uint8, device=dev)
+        md = torch.empty(mb.shape, dtype=torch.bfloat16, device=dev)
+        me = mb.size
+        breakdown["mx_small row-wise"] = timed(
+            lambda: check(lib.mxq_quantize_rowwise(P(m), mb.shape[0], mb.shape[1], mb.shape[1],
+                                                   P(mq), mb.shape[1], P(ms_), mb.shape[1] // 32,
+                                                   None, 0, sp), "rowwise"),
+            3 * me + me // 32)
+        breakdown["mx_small dequantize"] = timed(
+            lambda: check(lib.mxq_dequantize(P(mq), P(ms_), mb.shape[0], mb.shape[1], 1, P(md), sp),
+                          "dequantize"), 3 * me + me // 32)
+
+        # grouped MoE experts: 384 tensors, one launch
+        del x, qr, sr
+        torch.cuda.empty_cache()
+        shapes = workloads.moe_shapes()
+        mult = workloads.moe_multipliers()
+        log("generating moe_experts (384 tensors)")
+        xs = [workloads.moe_tensor(i, r, c, mult[i // 3], dev) for i, (_, r, c) in enumerate(shapes)]
+        outs = [(torch.empty((r, c), dtype=torch.uint8, device=dev),
+                 torch.empty((r, c // 32), dtype=torch.uint8, device=dev)) for (_, r, c) in shapes]
+        descs = (mxq.GroupDesc * len(xs))()
+        for i, (t, (q_, s_)) in enumerate(zip(xs, outs)):
+            descs[i] = mxq.GroupDesc(t.data_ptr(), q_.data_ptr(), s_.data_ptr(), t.shape[0],
+                                     t.shape[1], t.shape[1], t.shape[1], t.shape[1] // 32)
+        wsz = lib.mxq_grouped_workspace_size(len(xs))
+        gws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+        ge = sum(r * c for (_, r, c) in shapes)
+        breakdown["moe_experts grouped row-wise"] = timed(
+            lambda: check(lib.mxq_quantize_rowwise_grouped(descs, len(xs), P(gws), wsz, sp),
+                          "grouped"), 3 * ge + ge // 32, iters=10, flush_cache=False)
+        del xs, outs, gws
+        torch.cuda.empty_cache()
+
+        # square [8192, 8192]: block-FP8 and NVFP4, quantize and dequantize
+        yb = workloads.square_8192()
+        y = torch.from_numpy(yb.view(np.int16)).view(torch.bfloat16).to(dev)
+        n_ = yb.shape[0]
+        ye = yb.size
+        bq = torch.empty((n_, n_), dtype=torch.uint8, device=dev)
+        bS = torch.empty((n_ // 128, n_ // 128), dtype=torch.float32, device=dev)
+        bd = torch.empty((n_, n_), dtype=torch.bfloat16, device=dev)
+        breakdown["square_8192 block-FP8 quantize"] = timed(
+            lambda: check(lib.blockfp8_quantize(P(y), n_, n_, 128, P(bq), P(bS), sp), "bfp8"),
+            3 * ye + 4 * bS.numel())
+        breakdown["square_8192 block-FP8 dequantize"] = timed(
+            lambda: check(lib.blockfp8_dequantize(P(bq), P(bS), n_, n_, 128, P(bd), sp), "bfp8 dq"),
+            3 * ye + 4 * bS.numel())
+        nq = torch.empty((n_, n_ // 2), dtype=torch.uint8, device=dev)
+        ns = torch.empty((n_, n_ // 16), dtype=torch.uint8, device=dev)
+        ng = torch.empty((1,), dtype=torch.float32, device=dev)
+        nws = torch.empty((4,), dtype=torch.int32, device=dev)
+        breakdown["square_8192 NVFP4 quantize (unique bytes)"] = timed(
+            lambda: check(lib.nvfp4_quantize(P(y), n_, n_, P(nq), P(ns), P(ng), P(nws), 16, sp),
+                          "nvfp4"), 2 * ye + ye // 2 + ye // 16 + 4)
+        breakdown["square_8192 NVFP4 dequantize"] = timed(
+            lambda: check(lib.nvfp4_dequantize(P(nq), P(ns), P(ng), n_, n_, P(bd), sp), "nvfp4 dq"),
+            ye // 2 + ye // 16 + 4 + 2 * ye)
+        del flush
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "act_16384: bf16 [16384, 7168], 0.5*Student-t(3), seed 3; MXFP8 "
+                               "column-wise + row-wise + fused row-wise fake-quant in one pass",
+                   "rows": rows, "cols": cols, "bytes_per_step": step_bytes,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "copy_ceiling_GBs": round(copy_gbs, 1),
+        "breakdown": breakdown,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,299 @@
+// fp_kernels.hip -- block-FP8 (128 x 128 absmax, fp32 scale) and NVFP4
+// (global fp32 scale x per-16 E4M3 scale, E2M1 elements) for gfx950.
+//
+// Method (xorl PR #30 "Add FP8, NVFP4, and QARL training and export", deep
+// review, "What looked solid"): block-FP8 absmax scaling; NVFP4 two-level
+// global + FP8-block scaling with effective = block_scale * global_scale,
+// clamped (the E4M3 block scale saturates at 448) and zero blocks guarded;
+// FP4 output packed two per byte, [..., N/2] (miles PR #1372 "V4 mxfp4",
+// review of fp4_act_quant).  The steps the method defines in fp32 -- the
+// scale divisions, the element quotients and the dequantization products --
+// are single IEEE fp32 operations here, correctly rounded (HIP's default
+// fp32 division; no fast-math, denormals kept).
+#include <math.h>
+
+#include "launch.hpp"
+#include "mxq_device.hpp"
+
+namespace mxq {
+
+constexpr int kBlk = 128;   // block-FP8 tile edge
+constexpr int kSegNv = 512; // NVFP4 columns per wave segment (64 lanes x 8)
+constexpr int kRowsNv = 32; // NVFP4 rows per workgroup tile
+
+// ---------------------------------------------------------------------------
+// Block-FP8: one workgroup per 128 x 128 tile.  Thread t loads 8 rows
+// (t/16 + 16k) x 8 columns ((t%16)*8): each wave load covers 4 rows x 256 B.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restrict__ x,
+                                                         int64_t rows, int64_t cols,
+                                                         uint8_t *__restrict__ q,
+                                                         float *__restrict__ scale, int64_t tc)
+{
+    __shared__ uint32_t red[4];
+    const int64_t bi = blockIdx.x / tc, bj = blockIdx.x % tc;
+    const int tid = threadIdx.x;
+    const int64_t col = bj * kBlk + (tid & 15) * 8;
+    const int64_t rbase = bi * kBlk + (tid >> 4);
+    const bool cin = col < cols;  // cols % 8 == 0: a chunk is all in or all out
+
+    uint4 v[8];
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int64_t r = rbase + 16 * k;
+        v[k] = make_uint4(0, 0, 0, 0);
+        if (cin && r < rows) v[k] = *reinterpret_cast<const uint4 *>(x + r * cols + col);
+        m = max(m, amax8(v[k]));
+    }
+    m = wave_max(m);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+
+    const bool nonfinite = m >= 0x7F80u;
+    const float A = __uint_as_float(m << 16);      // exact: amax is a bf16 value
+    const float S = nonfinite ? __builtin_nanf("") : A / 448.0f;
+    const float div = (m == 0u) ? 1.0f : S;        // zero tile: codes are +-0
+    if (tid == 0) scale[bi * tc + bj] = S;
+
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int64_t r = rbase + 16 * k;
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        uint32_t c[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t w0 = w[2 * h], w1 = w[2 * h + 1];
+            const float f[4] = {bf16lo_to_f32(w0), bf16hi_to_f32(w0), bf16lo_to_f32(w1),
+                                bf16hi_to_f32(w1)};
+            uint32_t mags = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = __builtin_fabsf(f[j]) / div;   // one IEEE fp32 division
+                mags |= e4m3_mag_from_f32(t) << (8 * j);
+            }
+            mags = nonfinite ? 0x7F7F7F7Fu : mags;
+            c[h] = mags | signs4(w0, w1);
+        }
+        if (cin && r < rows) *reinterpret_cast<uint2 *>(q + r * cols + col) = make_uint2(c[0], c[1]);
+    }
+}
+
+// E4M3 code (with sign) to fp32, NaN for S.1111.111.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code)
+{
+    const uint32_t mag = code & 0x7Fu;
+    float v = e4m3_mag_value(mag);
+    v = mag == 0x7Fu ? __builtin_nanf("") : v;
+    return (code & 0x80u) ? -v : v;
+}
+
+// bf16 of an fp32 product; NaN -> quiet NaN with the element code's sign.
+__device__ __forceinline__ uint32_t bf16_of_product(float p, uint32_t code_sign)
+{
+    return p != p ? (0x7FC0u | (code_sign ? 0x8000u : 0u)) : bf16_rne(p);
+}
+
+__global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__restrict__ q,
+                                                           const float *__restrict__ scale,
+                                                           int64_t rows, int64_t cols,
+                                                           uint16_t *__restrict__ out, int64_t tc,
+                                                           int64_t nchunk)
+{
+    // Flat over 8-element chunks: chunk -> (row, col), cols % 8 == 0.
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nchunk) return;
+    const int64_t cpr = cols >> 3;
+    const int64_t r = i / cpr;
+    const int64_t col = (i - r * cpr) * 8;
+    const float S = scale[(r / kBlk) * tc + col / kBlk];
+    const uint2 c = *reinterpret_cast<const uint2 *>(q + r * cols + col);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        const uint32_t cw = j < 4 ? c.x : c.y;
+        const int sh = 8 * (j & 3);
+        const uint32_t c0 = (cw >> sh) & 0xFFu, c1 = (cw >> (sh + 8)) & 0xFFu;
+        const float p0 = e4m3_to_f32(c0) * S;   // one IEEE fp32 multiplication
+        const float p1 = e4m3_to_f32(c1) * S;
+        o[j / 2] = bf16_of_product(p0, c0 & 0x80u) | (bf16_of_product(p1, c1 & 0x80u) << 16);
+    }
+    *reinterpret_cast<uint4 *>(out + r * cols + col) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4.  Pass 1: tensor-wide max magnitude (bf16 bits, an unsigned max, so
+// the atomic reduction is order-independent and deterministic).  Pass 2:
+// scales and E2M1 codes; a 16-block is 2 adjacent lanes x 8 values.
+// ---------------------------------------------------------------------------
+__global__ void nvfp4_zero_kernel(uint32_t *ws) { ws[0] = 0u; }
+
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
+                                                         int64_t nvec, uint32_t *ws)
+{
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride)
+        m = max(m, amax8(reinterpret_cast<const uint4 *>(x)[i]));
+    m = wave_max(m);
+    if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(ws, m);
+}
+
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t rows, int64_t cols,
+                                                          uint8_t *__restrict__ q,
+                                                          uint8_t *__restrict__ s_out,
+                                                          float *__restrict__ g_out,
+                                                          const uint32_t *__restrict__ ws,
+                                                          int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSegNv + lane * 8;
+    const bool cin = col < cols;  // cols % 16 == 0: a lane pair is all in or all out
+
+    const uint32_t am = ws[0];
+    const bool nonfinite = am >= 0x7F80u;
+    const float A = __uint_as_float(am << 16);
+    const float g = A / 2688.0f;                 // 2688 = 448 * 6
+    const float d = 6.0f * g;
+    if (tile == 0 && threadIdx.x == 0) *g_out = nonfinite ? __builtin_nanf("") : g;
+
+    for (int i = 0; i < kRowsNv / 4; ++i) {
+        const int64_t r = rb * kRowsNv + wave + 4 * i;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        const bool ok = cin && r < rows;
+        if (ok) v = *reinterpret_cast<const uint4 *>(x + r * cols + col);
+        const uint32_t b8 = amax8(v);
+        const uint32_t b = max(b8, dpp_swap1(b8));        // amax of the 16-block
+        uint32_t s;
+        if (nonfinite) {
+            s = 0x7Fu;
+        } else if (g == 0.0f) {
+            s = 0u;
+        } else {
+            const float ratio = __uint_as_float(b << 16) / d;  // one IEEE fp32 division
+            s = e4m3_mag_from_f32(ratio);
+        }
+        const float eff = e4m3_mag_value(s & 0x7Fu) * g;       // one IEEE fp32 multiplication
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float f0 = bf16lo_to_f32(w[j]), f1 = bf16hi_to_f32(w[j]);
+            uint32_t n0, n1;
+            if (nonfinite) {
+                n0 = n1 = 7u;
+            } else if (eff == 0.0f) {
+                n0 = n1 = 0u;
+            } else {
+                n0 = e2m1_mag_from_f32(__builtin_fabsf(f0) / eff);   // one IEEE fp32 division
+                n1 = e2m1_mag_from_f32(__builtin_fabsf(f1) / eff);
+            }
+            n0 |= (w[j] >> 12) & 0x8u;          // sign of the low bf16
+            n1 |= (w[j] >> 28) & 0x8u;          // sign of the high bf16
+            packed |= (n0 | (n1 << 4)) << (8 * j);
+        }
+        if (ok) {
+            *reinterpret_cast<uint32_t *>(q + r * (cols >> 1) + (col >> 1)) = packed;
+            if ((lane & 1) == 0) s_out[r * (cols >> 4) + (col >> 4)] = (uint8_t)s;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__restrict__ q,
+                                                            const uint8_t *__restrict__ s_in,
+                                                            const float *__restrict__ g_in,
+                                                            int64_t rows, int64_t cols,
+                                                            uint16_t *__restrict__ out,
+                                                            int64_t nchunk)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nchunk) return;
+    const int64_t cpr = cols >> 3;
+    const int64_t r = i / cpr;
+    const int64_t col = (i - r * cpr) * 8;
+    const float g = *g_in;
+    const uint32_t sb = s_in[r * (cols >> 4) + (col >> 4)];
+    const float eff = e4m3_to_f32(sb) * g;                 // one IEEE fp32 multiplication
+    const uint32_t packed = *reinterpret_cast<const uint32_t *>(q + r * (cols >> 1) + (col >> 1));
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t byte = (packed >> (8 * j)) & 0xFFu;
+        const uint32_t n0 = byte & 0xFu, n1 = byte >> 4;
+        float v0 = e2m1_mag_value(n0 & 7u), v1 = e2m1_mag_value(n1 & 7u);
+        v0 = (n0 & 8u) ? -v0 : v0;
+        v1 = (n1 & 8u) ? -v1 : v1;
+        const float p0 = v0 * eff, p1 = v1 * eff;         // one IEEE fp32 multiplication each
+        o[j] = bf16_of_product(p0, n0 & 8u) | (bf16_of_product(p1, n1 & 8u) << 16);
+    }
+    *reinterpret_cast<uint4 *>(out + r * cols + col) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                             float *scale, hipStream_t stream)
+{
+    const int64_t tr = (rows + kBlk - 1) / kBlk, tc = (cols + kBlk - 1) / kBlk;
+    if (tr * tc <= 0) return hipSuccess;
+    if (tr * tc > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bfp8_quant_kernel, dim3((unsigned)(tr * tc)), dim3(256), 0, stream, x, rows,
+                       cols, q, scale, tc);
+    return hipGetLastError();
+}
+
+hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                               uint16_t *out, hipStream_t stream)
+{
+    const int64_t nchunk = rows * (cols / 8);
+    if (nchunk <= 0) return hipSuccess;
+    const int64_t blocks = (nchunk + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const int64_t tc = (cols + kBlk - 1) / kBlk;
+    hipLaunchKernelGGL(bfp8_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, scale,
+                       rows, cols, out, tc, nchunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                              uint8_t *s, float *g, uint32_t *ws, hipStream_t stream)
+{
+    const int64_t nvec = rows * cols / 8;
+    if (nvec <= 0) return hipSuccess;
+    hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(1), 0, stream, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t want = (nvec + 255) / 256;
+    const int64_t ablocks = want < 4096 ? want : 4096;
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
+    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,
+                       cols, q, s, g, ws, nseg);
+    return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *g, int64_t rows,
+                                int64_t cols, uint16_t *out, hipStream_t stream)
+{
+    const int64_t nchunk = rows * (cols / 8);
+    if (nchunk <= 0) return hipSuccess;
+    const int64_t blocks = (nchunk + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, s, g,
+                       rows, cols, out, nchunk);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,0 +1,48 @@
+// launch.hpp -- host-side launchers of the gfx950 kernels (internal).
+// Arguments arrive already validated by the C ABI layer (mxq_abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+// Launch table entry for the grouped row-wise kernel (staged in the caller's
+// device workspace).  `tile_begin` is the first tile index of the tensor in
+// the flattened tile space; tiles are (512-column segment, 32-row block).
+struct GroupEntry {
+    const uint16_t *x;
+    uint8_t *q;
+    uint8_t *scale;
+    int64_t rows, cols, ldx, ldq, lds;
+    int64_t tile_begin;
+    int64_t nseg;  // 512-column segments per row block
+};
+
+hipError_t launch_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t *q, int64_t ldq, uint8_t *scale, int64_t lds,
+                             uint16_t *fq, int64_t ldf, hipStream_t stream);
+
+hipError_t launch_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qc,
+                             uint8_t *sc, uint8_t *qr, uint8_t *sr, uint16_t *fq_row,
+                             uint16_t *fq_col, hipStream_t stream);
+
+hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
+                             int axis, uint16_t *out, hipStream_t stream);
+
+hipError_t launch_mx_grouped(const GroupEntry *table_dev, int32_t n, int64_t total_tiles,
+                             hipStream_t stream);
+
+int64_t mx_row_tiles(int64_t rows, int64_t cols, int64_t *nseg);
+
+hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                             float *scale, hipStream_t stream);
+hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                               uint16_t *out, hipStream_t stream);
+
+hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                              uint8_t *s, float *g, uint32_t *ws, hipStream_t stream);
+hipError_t launch_nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *g,
+                                int64_t rows, int64_t cols, uint16_t *out, hipStream_t stream);
+
+}  // namespace mxq

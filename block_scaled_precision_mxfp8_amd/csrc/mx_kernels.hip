@@ -1,0 +1,354 @@
+// mx_kernels.hip -- MXFP8 kernels for gfx950: row-wise quantize (+ fused
+// fake-quant), one-pass column-wise + row-wise + fake-quant, dequantize, and
+// the grouped row-wise launch over many tensors.
+//
+// Method ("PR #1935 完整报告 / Use TransformerEngine for MXFP8 quantization",
+// section 实现拆解 item 1): groups of 32 consecutive values share one
+// power-of-two E8M0 scale; elements are E4M3 codes; outputs are compact and
+// non-swizzled.  Rows need no padding: row groups never span rows, so the
+// zero-pad-to-32-rows-then-crop route gives the same bytes as predicating the
+// missing rows off, which is what the kernels do.
+//
+// Work layout.  A wave owns a 512-column segment (64 lanes x 8 bf16 = one
+// 16-byte load per lane, 1 KiB contiguous per load instruction) of a run of
+// rows.  A row group of 32 is 4 adjacent lanes, so its amax is two DPP
+// steps; a column group of 32 is 32 rows of the same lane, so its amax stays
+// in the lane.  All of this is HBM streaming: there is no reuse across
+// workgroups, so the blockIdx -> tile order only keeps each workgroup's
+// accesses contiguous.
+#include "launch.hpp"
+#include "mxq_device.hpp"
+
+namespace mxq {
+
+constexpr int kSeg = 512;          // columns per wave segment
+constexpr int kRowsPerTile = 32;   // rows per row-wise workgroup tile (4 waves x 8 rows)
+constexpr int kU = 4;              // rows each wave keeps in flight per step
+constexpr int kColTileRows = 128;  // rows per column-wise workgroup tile (4 waves x 32)
+
+// ---------------------------------------------------------------------------
+// Row-wise tile: rows [rb*32, rb*32+32) x columns of segment `seg`.
+// ---------------------------------------------------------------------------
+template <bool kQ, bool kFQ>
+__device__ __forceinline__ void mx_row_tile(const uint16_t *__restrict__ x, int64_t rows,
+                                            int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
+                                            int64_t ldq, uint8_t *__restrict__ scale, int64_t lds,
+                                            uint16_t *__restrict__ fq, int64_t ldf, int64_t seg,
+                                            int64_t rb)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSeg + lane * 8;
+    const bool cin = col < cols;  // cols % 32 == 0: a quad is all in or all out
+    const int64_t r0 = rb * kRowsPerTile + wave;
+
+#pragma unroll
+    for (int it = 0; it < kRowsPerTile / (4 * kU); ++it) {
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t r = r0 + 4 * (it * kU + u);
+            v[u] = make_uint4(0, 0, 0, 0);
+            if (cin && r < rows) v[u] = *reinterpret_cast<const uint4 *>(x + r * ldx + col);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t r = r0 + 4 * (it * kU + u);
+            const bool ok = cin && r < rows;
+            const uint32_t s = mx_scale_byte(quad_max(amax8(v[u])));
+            const bool nan_group = s == 0xFFu;
+            const int e = 7 - (int)s;
+            const uint32_t c0 = e4m3x4_row(v[u].x, v[u].y, e, nan_group);
+            const uint32_t c1 = e4m3x4_row(v[u].z, v[u].w, e, nan_group);
+            if (kQ && ok) {
+                *reinterpret_cast<uint2 *>(q + r * ldq + col) = make_uint2(c0, c1);
+                if ((lane & 3) == 0) scale[r * lds + (col >> 5)] = (uint8_t)s;
+            }
+            if (kFQ) {
+                const int edq = (int)s - 7;
+                const uint2 lo = mx_dequant4(c0, edq, nan_group);
+                const uint2 hi = mx_dequant4(c1, edq, nan_group);
+                if (ok) *reinterpret_cast<uint4 *>(fq + r * ldf + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+    }
+}
+
+template <bool kQ, bool kFQ>
+__global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restrict__ x,
+                                                         int64_t rows, int64_t cols, int64_t ldx,
+                                                         uint8_t *__restrict__ q, int64_t ldq,
+                                                         uint8_t *__restrict__ scale, int64_t lds,
+                                                         uint16_t *__restrict__ fq, int64_t ldf,
+                                                         int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    mx_row_tile<kQ, kFQ>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, tile % nseg, tile / nseg);
+}
+
+// ---------------------------------------------------------------------------
+// Column-wise (+ row-wise + fake-quant) in one read of x.  A wave holds one
+// 32-row group x 512 columns in registers (32 x 16 bytes per lane): the column
+// amax is an in-lane max over the 32 loads, the row amax a quad max per row.
+// ---------------------------------------------------------------------------
+template <bool kCol, bool kRow, bool kFQRow, bool kFQCol>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mx_colwise_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qc,
+    uint8_t *__restrict__ sc, uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
+    uint16_t *__restrict__ fq_row, uint16_t *__restrict__ fq_col, int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSeg + lane * 8;
+    const bool cin = col < cols;
+    const int64_t g = rb * (kColTileRows / 32) + wave;  // 32-row group index
+    const int64_t r0 = g * 32;
+    if (r0 >= rows) return;  // wave-uniform; the kernel has no barriers
+
+    uint4 v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (cin && r0 + i < rows) v[i] = *reinterpret_cast<const uint4 *>(x + (r0 + i) * cols + col);
+    }
+
+    if (kCol || kFQCol) {
+        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            m0 = pk_max_u16(m0, mag2(v[i].x));
+            m1 = pk_max_u16(m1, mag2(v[i].y));
+            m2 = pk_max_u16(m2, mag2(v[i].z));
+            m3 = pk_max_u16(m3, mag2(v[i].w));
+        }
+        const uint32_t am[8] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16,
+                                m2 & 0xFFFFu, m2 >> 16, m3 & 0xFFFFu, m3 >> 16};
+        uint32_t s[8];
+        int e[8], edq[8];
+        bool nan[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            s[j] = mx_scale_byte(am[j]);
+            nan[j] = s[j] == 0xFFu;
+            e[j] = 7 - (int)s[j];
+            edq[j] = (int)s[j] - 7;
+        }
+        if (kCol && cin) {
+            const uint32_t lo = s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24);
+            const uint32_t hi = s[4] | (s[5] << 8) | (s[6] << 16) | (s[7] << 24);
+            *reinterpret_cast<uint2 *>(sc + g * cols + col) = make_uint2(lo, hi);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int64_t r = r0 + i;
+            const bool ok = cin && r < rows;
+            const uint32_t c0 = e4m3x4_col(v[i].x, v[i].y, e, nan);
+            const uint32_t c1 = e4m3x4_col(v[i].z, v[i].w, e + 4, nan + 4);
+            if (kCol && ok) *reinterpret_cast<uint2 *>(qc + r * cols + col) = make_uint2(c0, c1);
+            if (kFQCol) {
+                uint32_t b[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    b[j] = mx_dequant1((c0 >> (8 * j)) & 0xFFu, edq[j], nan[j]);
+                    b[4 + j] = mx_dequant1((c1 >> (8 * j)) & 0xFFu, edq[4 + j], nan[4 + j]);
+                }
+                if (ok)
+                    *reinterpret_cast<uint4 *>(fq_col + r * cols + col) =
+                        make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                                   b[6] | (b[7] << 16));
+            }
+        }
+    }
+
+    if (kRow || kFQRow) {
+        const int64_t ngr = cols >> 5;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int64_t r = r0 + i;
+            const bool ok = cin && r < rows;
+            const uint32_t s = mx_scale_byte(quad_max(amax8(v[i])));
+            const bool nan_group = s == 0xFFu;
+            const int e = 7 - (int)s;
+            const uint32_t c0 = e4m3x4_row(v[i].x, v[i].y, e, nan_group);
+            const uint32_t c1 = e4m3x4_row(v[i].z, v[i].w, e, nan_group);
+            if (kRow && ok) {
+                *reinterpret_cast<uint2 *>(qr + r * cols + col) = make_uint2(c0, c1);
+                if ((lane & 3) == 0) sr[r * ngr + (col >> 5)] = (uint8_t)s;
+            }
+            if (kFQRow) {
+                const int edq = (int)s - 7;
+                const uint2 lo = mx_dequant4(c0, edq, nan_group);
+                const uint2 hi = mx_dequant4(c1, edq, nan_group);
+                if (ok)
+                    *reinterpret_cast<uint4 *>(fq_row + r * cols + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: out = bf16_RNE(E4M3(q) * 2^(s - 127)), row (axis 1) or column
+// (axis 0) groups.  Tiles as the row-wise kernel.
+// ---------------------------------------------------------------------------
+template <int kAxis>
+__global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restrict__ q,
+                                                         const uint8_t *__restrict__ scale,
+                                                         int64_t rows, int64_t cols,
+                                                         uint16_t *__restrict__ out, int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSeg + lane * 8;
+    if (col >= cols) return;  // no barriers below
+    const int64_t r0 = rb * kRowsPerTile + wave;
+#pragma unroll
+    for (int i = 0; i < kRowsPerTile / 4; ++i) {
+        const int64_t r = r0 + 4 * i;
+        if (r >= rows) break;
+        const uint2 c = *reinterpret_cast<const uint2 *>(q + r * cols + col);
+        uint32_t b[8];
+        if (kAxis == 1) {
+            const uint32_t s = scale[r * (cols >> 5) + (col >> 5)];
+            const bool nan = s == 0xFFu;
+            const uint2 lo = mx_dequant4(c.x, (int)s - 7, nan);
+            const uint2 hi = mx_dequant4(c.y, (int)s - 7, nan);
+            b[0] = lo.x; b[1] = lo.y; b[2] = hi.x; b[3] = hi.y;
+        } else {
+            const uint2 sv = *reinterpret_cast<const uint2 *>(scale + (r >> 5) * cols + col);
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                const uint32_t cw = j < 4 ? c.x : c.y;
+                const uint32_t sw = j < 4 ? sv.x : sv.y;
+                const int sh = 8 * (j & 3);
+                const uint32_t s0 = (sw >> sh) & 0xFFu, s1 = (sw >> (sh + 8)) & 0xFFu;
+                const uint32_t d0 = mx_dequant1((cw >> sh) & 0xFFu, (int)s0 - 7, s0 == 0xFFu);
+                const uint32_t d1 = mx_dequant1((cw >> (sh + 8)) & 0xFFu, (int)s1 - 7, s1 == 0xFFu);
+                w[j / 2] = d0 | (d1 << 16);
+            }
+            b[0] = w[0]; b[1] = w[1]; b[2] = w[2]; b[3] = w[3];
+        }
+        *reinterpret_cast<uint4 *>(out + r * cols + col) = make_uint4(b[0], b[1], b[2], b[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped row-wise: a persistent grid; each workgroup takes a contiguous run
+// of tiles of the flattened (tensor, tile) space, finds its first tensor by
+// binary search over tile_begin and walks forward.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mx_grouped_kernel(const GroupEntry *__restrict__ table,
+                                                         int32_t n, int64_t total_tiles,
+                                                         int64_t tiles_per_block)
+{
+    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_block;
+    const int64_t t1 = min(t0 + tiles_per_block, total_tiles);
+    if (t0 >= t1) return;
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (table[mid].tile_begin <= t0) lo = mid;
+        else hi = mid - 1;
+    }
+    int e = lo;
+    for (int64_t t = t0; t < t1; ++t) {
+        while (e + 1 < n && table[e + 1].tile_begin <= t) ++e;
+        const GroupEntry E = table[e];
+        const int64_t local = t - E.tile_begin;
+        mx_row_tile<true, false>(E.x, E.rows, E.cols, E.ldx, E.q, E.ldq, E.scale, E.lds, nullptr,
+                                 0, local % E.nseg, local / E.nseg);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+int64_t mx_row_tiles(int64_t rows, int64_t cols, int64_t *nseg)
+{
+    const int64_t ns = (cols + kSeg - 1) / kSeg;
+    if (nseg) *nseg = ns;
+    return ns * ((rows + kRowsPerTile - 1) / kRowsPerTile);
+}
+
+hipError_t launch_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t *q, int64_t ldq, uint8_t *scale, int64_t lds, uint16_t *fq,
+                             int64_t ldf, hipStream_t stream)
+{
+    int64_t nseg = 0;
+    const int64_t tiles = mx_row_tiles(rows, cols, &nseg);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)tiles), block(256);
+    if (q && fq)
+        hipLaunchKernelGGL((mx_rowwise_kernel<true, true>), grid, block, 0, stream, x, rows, cols,
+                           ldx, q, ldq, scale, lds, fq, ldf, nseg);
+    else if (q)
+        hipLaunchKernelGGL((mx_rowwise_kernel<true, false>), grid, block, 0, stream, x, rows, cols,
+                           ldx, q, ldq, scale, lds, fq, ldf, nseg);
+    else
+        hipLaunchKernelGGL((mx_rowwise_kernel<false, true>), grid, block, 0, stream, x, rows, cols,
+                           ldx, q, ldq, scale, lds, fq, ldf, nseg);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qc,
+                             uint8_t *sc, uint8_t *qr, uint8_t *sr, uint16_t *fq_row,
+                             uint16_t *fq_col, hipStream_t stream)
+{
+    const int64_t nseg = (cols + kSeg - 1) / kSeg;
+    const int64_t tiles = nseg * ((rows + kColTileRows - 1) / kColTileRows);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)tiles), block(256);
+    const bool col = qc != nullptr, row = qr != nullptr;
+#define MXQ_COLWISE(C, R, FR, FC)                                                                  \
+    hipLaunchKernelGGL((mx_colwise_kernel<C, R, FR, FC>), grid, block, 0, stream, x, rows, cols,   \
+                       qc, sc, qr, sr, fq_row, fq_col, nseg)
+    if (col && row && fq_row) MXQ_COLWISE(true, true, true, false);
+    else if (col && row) MXQ_COLWISE(true, true, false, false);
+    else if (col && fq_row) MXQ_COLWISE(true, false, true, false);
+    else if (col) MXQ_COLWISE(true, false, false, false);
+    else if (fq_col) MXQ_COLWISE(false, false, false, true);
+    else return hipErrorInvalidValue;
+#undef MXQ_COLWISE
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
+                             int axis, uint16_t *out, hipStream_t stream)
+{
+    int64_t nseg = 0;
+    const int64_t tiles = mx_row_tiles(rows, cols, &nseg);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)tiles), block(256);
+    if (axis == 1)
+        hipLaunchKernelGGL((mx_dequant_kernel<1>), grid, block, 0, stream, q, scale, rows, cols,
+                           out, nseg);
+    else
+        hipLaunchKernelGGL((mx_dequant_kernel<0>), grid, block, 0, stream, q, scale, rows, cols,
+                           out, nseg);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_grouped(const GroupEntry *table_dev, int32_t n, int64_t total_tiles,
+                             hipStream_t stream)
+{
+    if (n <= 0 || total_tiles <= 0) return hipSuccess;
+    // 8 resident 256-thread workgroups per CU on 256 CUs.
+    const int64_t max_blocks = 2048;
+    const int64_t blocks = total_tiles < max_blocks ? total_tiles : max_blocks;
+    const int64_t per = (total_tiles + blocks - 1) / blocks;
+    hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, table_dev,
+                       n, total_tiles, per);
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,0 +1,235 @@
+// mxq_abi.hip -- the extern "C" entry points declared in include/mxq.h.
+//
+// Every argument is checked on the host before anything is launched, so a
+// rejected call has no side effect and every error path can be exercised
+// without a GPU.  A failure is always reported, never downgraded to another
+// code path (the fail-visible rule the pages argue for: fusion-mlx issue #425
+// keeps its explicit raise instead of a silent downgrade, and the xorl PR #30
+// review objects to a swallowed RuntimeError that hides a broken fast path).
+#include <string.h>
+
+#include <vector>
+
+#include "launch.hpp"
+#include "mxq.h"
+
+using mxq::GroupEntry;
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// rows * ld + cols fits int64 (all kernels index with int64).
+inline bool fits(int64_t rows, int64_t ld)
+{
+    int64_t t;
+    return !__builtin_mul_overflow(rows, ld, &t);
+}
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline mxq_status from_hip(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_EHIP; }
+
+mxq_status check_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                         const uint8_t *q, int64_t ldq, const uint8_t *scale, int64_t lds,
+                         const uint16_t *fq, int64_t ldf, bool need_q)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || (need_q && (!q || !scale)) || (!need_q && !fq)) return MXQ_EINVAL;
+    if (ldx < cols) return MXQ_ESHAPE;
+    if (!aligned(x, 16) || ldx % 8 != 0) return MXQ_EALIGN;
+    if (q) {
+        if (!scale) return MXQ_EINVAL;
+        if (ldq < cols || lds < cols / 32) return MXQ_ESHAPE;
+        if (!aligned(q, 8) || ldq % 8 != 0) return MXQ_EALIGN;
+        if (!fits(rows, ldq) || !fits(rows, lds)) return MXQ_ESIZE;
+    }
+    if (fq) {
+        if (ldf < cols) return MXQ_ESHAPE;
+        if (!aligned(fq, 16) || ldf % 8 != 0) return MXQ_EALIGN;
+        if (!fits(rows, ldf)) return MXQ_ESIZE;
+    }
+    if (!fits(rows, ldx)) return MXQ_ESIZE;
+    return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mxq_status_string(int status)
+{
+    switch (status) {
+    case MXQ_OK: return "ok";
+    case MXQ_EINVAL: return "invalid argument (null pointer, negative size or bad axis)";
+    case MXQ_ESHAPE: return "unsupported shape (group/block divisibility or leading dimension)";
+    case MXQ_EALIGN: return "misaligned pointer or leading dimension";
+    case MXQ_EHIP: return "HIP runtime error at launch";
+    case MXQ_ESIZE: return "workspace too small or size overflow";
+    default: return "unknown status";
+    }
+}
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+mxq_status mxq_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t *q, int64_t ldq, uint8_t *scale, int64_t lds,
+                                uint16_t *fq, int64_t ldf, void *stream)
+{
+    mxq_status st = check_rowwise(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, true);
+    if (st != MXQ_OK || rows == 0 || cols == 0) return st;
+    return from_hip(mxq::launch_mx_rowwise(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf,
+                                           as_stream(stream)));
+}
+
+mxq_status mxq_quantize_colwise(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qc,
+                                uint8_t *sc, uint8_t *qr, uint8_t *sr, uint16_t *fq, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !qc || !sc) return MXQ_EINVAL;
+    if ((qr == nullptr) != (sr == nullptr)) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(qc, 8) || !aligned(sc, 8)) return MXQ_EALIGN;
+    if (qr && !aligned(qr, 8)) return MXQ_EALIGN;
+    if (fq && !aligned(fq, 16)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_mx_colwise(x, rows, cols, qc, sc, qr, sr, fq, nullptr,
+                                           as_stream(stream)));
+}
+
+mxq_status mxq_dequantize(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
+                          int axis, uint16_t *out, void *stream)
+{
+    if (rows < 0 || cols < 0 || (axis != 0 && axis != 1)) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!q || !scale || !out) return MXQ_EINVAL;
+    if (!aligned(q, 8) || !aligned(out, 16)) return MXQ_EALIGN;
+    if (axis == 0 && !aligned(scale, 8)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_mx_dequant(q, scale, rows, cols, axis, out, as_stream(stream)));
+}
+
+mxq_status mxq_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint16_t *out,
+                          void *stream)
+{
+    if (rows < 0 || cols < 0 || (axis != 0 && axis != 1)) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !out) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(out, 16)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    hipError_t e;
+    if (axis == 1)
+        e = mxq::launch_mx_rowwise(x, rows, cols, cols, nullptr, 0, nullptr, 0, out, cols,
+                                   as_stream(stream));
+    else
+        e = mxq::launch_mx_colwise(x, rows, cols, nullptr, nullptr, nullptr, nullptr, nullptr, out,
+                                   as_stream(stream));
+    return from_hip(e);
+}
+
+size_t mxq_grouped_workspace_size(int32_t n)
+{
+    return n <= 0 ? 0 : (size_t)n * sizeof(GroupEntry);
+}
+
+mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n, void *workspace,
+                                        size_t workspace_bytes, void *stream)
+{
+    if (n < 0) return MXQ_EINVAL;
+    if (n == 0) return MXQ_OK;
+    if (!descs || !workspace) return MXQ_EINVAL;
+    if (!aligned(workspace, 16)) return MXQ_EALIGN;
+    if (workspace_bytes < mxq_grouped_workspace_size(n)) return MXQ_ESIZE;
+    std::vector<GroupEntry> table;
+    table.reserve((size_t)n);
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const mxq_group_desc &d = descs[i];
+        mxq_status st = check_rowwise(d.x, d.rows, d.cols, d.ldx, d.q, d.ldq, d.scale, d.lds,
+                                      nullptr, 0, true);
+        if (st != MXQ_OK) return st;
+        if (d.rows == 0 || d.cols == 0) continue;
+        GroupEntry e;
+        e.x = d.x;
+        e.q = d.q;
+        e.scale = d.scale;
+        e.rows = d.rows;
+        e.cols = d.cols;
+        e.ldx = d.ldx;
+        e.ldq = d.ldq;
+        e.lds = d.lds;
+        e.tile_begin = tiles;
+        const int64_t t = mxq::mx_row_tiles(d.rows, d.cols, &e.nseg);
+        if (__builtin_add_overflow(tiles, t, &tiles)) return MXQ_ESIZE;
+        table.push_back(e);
+    }
+    if (table.empty()) return MXQ_OK;
+    // Pageable source: the copy has consumed `table` by the time it returns.
+    hipError_t err = hipMemcpyAsync(workspace, table.data(), table.size() * sizeof(GroupEntry),
+                                    hipMemcpyHostToDevice, as_stream(stream));
+    if (err != hipSuccess) return MXQ_EHIP;
+    return from_hip(mxq::launch_mx_grouped(static_cast<const GroupEntry *>(workspace),
+                                           (int32_t)table.size(), tiles, as_stream(stream)));
+}
+
+mxq_status blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int32_t blk,
+                             uint8_t *q, float *scale, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (blk != 128 || cols % 8 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !q || !scale) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_quant(x, rows, cols, q, scale, as_stream(stream)));
+}
+
+mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                               int32_t blk, uint16_t *out, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (blk != 128 || cols % 8 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!q || !scale || !out) return MXQ_EINVAL;
+    if (!aligned(q, 8) || !aligned(out, 16) || !aligned(scale, 4)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_dequant(q, scale, rows, cols, out, as_stream(stream)));
+}
+
+mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
+                          uint8_t *s_e4m3, float *global_scale, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 16 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !q_packed || !s_e4m3 || !global_scale || !workspace) return MXQ_EINVAL;
+    if (workspace_bytes < 4) return MXQ_ESIZE;
+    if (!aligned(x, 16) || !aligned(q_packed, 4) || !aligned(global_scale, 4) ||
+        !aligned(workspace, 4))
+        return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_nvfp4_quant(x, rows, cols, q_packed, s_e4m3, global_scale,
+                                            static_cast<uint32_t *>(workspace), as_stream(stream)));
+}
+
+mxq_status nvfp4_dequantize(const uint8_t *q_packed, const uint8_t *s_e4m3,
+                            const float *global_scale, int64_t rows, int64_t cols, uint16_t *out,
+                            void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 16 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!q_packed || !s_e4m3 || !global_scale || !out) return MXQ_EINVAL;
+    if (!aligned(q_packed, 4) || !aligned(out, 16) || !aligned(global_scale, 4)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_nvfp4_dequant(q_packed, s_e4m3, global_scale, rows, cols, out,
+                                              as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,202 @@
+/*
+ * mxq.h -- C ABI of the MI355X (gfx950) block-scaled quantization library.
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *   - MXFP8: every group of 32 consecutive values shares one power-of-two
+ *     scale stored as an E8M0 byte; the values are cast to FP8 E4M3.  The
+ *     output is a compact, non-swizzled qweight plus a scale tensor, the one
+ *     a checkpoint stores as `<name>.weight_scale_inv`, and rows that are not a
+ *     multiple of 32 behave exactly as the zero-pad-then-crop route ("PR #1935
+ *     完整报告 / Use TransformerEngine for MXFP8 quantization", section 实现拆解
+ *     item 1 and 关键源码片段).  Power-of-two scales and the E8M0 scale dtype:
+ *     miles PR #1372 "V4 mxfp4", PR description.  The scale exponent is
+ *     floor(log2 amax) - 8 (the OCP microscaling conversion for E4M3, whose
+ *     largest power of two is 2^8); elements round to nearest even and
+ *     saturate at +-448.
+ *   - Fake quantization (quantize, then dequantize back to bf16) for
+ *     simulated QAT: miles PR #1372 "V4 mxfp4", the compressor review.
+ *   - Block-FP8 (128 x 128 absmax, fp32 scale) and NVFP4 (global fp32 scale x
+ *     per-16 E4M3 scale, E2M1 elements packed two per byte): xorl PR #30 "Add
+ *     FP8, NVFP4, and QARL training and export", deep review, "What looked
+ *     solid"; the packed FP4 output shape [..., N/2] from the review of
+ *     fp4_act_quant in miles PR #1372.
+ *
+ * Conventions for every entry point
+ *   - Data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronizes; every call is asynchronous on
+ *     `stream` (a hipStream_t passed as void*, NULL = the default stream).
+ *   - bf16 tensors are passed as uint16_t bit patterns; E4M3, E8M0 and packed
+ *     E2M1 codes as uint8_t; fp32 scales as float.  All are row-major.
+ *   - Arguments are checked on the host before anything is launched; a
+ *     rejected call launches nothing and writes nothing.  A launch the HIP
+ *     runtime refuses returns MXQ_EHIP.  Faults that happen on the device
+ *     surface at the caller's next synchronization.
+ *   - Outputs are fully overwritten; no byte outside them is written.
+ *   - rows == 0 is accepted and launches nothing (all pointers may then be
+ *     NULL).  Sizes must satisfy the per-call shape rules and fit int64.
+ *   - The library keeps no state: calls from several host threads are safe.
+ *   - Non-finite inputs: an MX group, block-FP8 tile or NVFP4 tensor that
+ *     holds NaN or Inf is quantized as all-NaN (E8M0 byte 0xFF / fp32 NaN
+ *     scale / E4M3 0x7F with each element's sign; NVFP4, whose E2M1 has no
+ *     NaN: global scale NaN, block scales 0x7F, nibbles 0x7 with the sign).
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+typedef enum mxq_status {
+    MXQ_OK = 0,
+    MXQ_EINVAL = 1, /* NULL pointer where one is needed, negative size, bad axis */
+    MXQ_ESHAPE = 2, /* shape the operation does not accept (e.g. cols % 32 != 0) */
+    MXQ_EALIGN = 3, /* pointer or leading dimension misaligned for vector access */
+    MXQ_EHIP = 4,   /* the HIP runtime rejected a launch or copy */
+    MXQ_ESIZE = 5   /* workspace too small, or a size overflows the index type */
+} mxq_status;
+
+/* Static English text for a status code (never NULL). */
+const char *mxq_status_string(int status);
+
+/* MXQ_ABI_VERSION of the built library. */
+int mxq_abi_version(void);
+
+/*
+ * Row-wise MXFP8 quantization ("PR #1935 完整报告", 实现拆解 item 1).
+ *   x      [rows, cols] bf16, row stride ldx elements
+ *   q      [rows, cols] E4M3 codes, row stride ldq bytes
+ *   scale  [rows, cols/32] E8M0 bytes, row stride lds bytes (weight_scale_inv)
+ *   fq     optional [rows, cols] bf16 fake-quant output (dequantize(q, scale)),
+ *          row stride ldf elements; NULL to skip
+ * Shape: cols % 32 == 0 (MXQ_ESHAPE otherwise); any rows >= 0.  Rows need no
+ * padding: the result equals zero-padding to a multiple of 32 rows and
+ * cropping back.  ldx >= cols, ldq >= cols, lds >= cols/32, ldf >= cols.
+ * Alignment (MXQ_EALIGN): x and fq 16-byte aligned with ldx, ldf multiples of
+ * 8; q 8-byte aligned with ldq a multiple of 8.
+ */
+mxq_status mxq_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t *q, int64_t ldq, uint8_t *scale, int64_t lds,
+                                uint16_t *fq, int64_t ldf, void *stream);
+
+/*
+ * Column-wise MXFP8 quantization: groups of 32 consecutive rows within each
+ * column (the token axis of an activation [tokens, hidden]).  One pass over x
+ * can also produce the row-wise result and the row-wise fake-quant.
+ *   x      [rows, cols] bf16, contiguous
+ *   qc     [rows, cols] E4M3 codes in x's layout, contiguous
+ *   sc     [ceil(rows/32), cols] E8M0 bytes, contiguous; a last group of
+ *          fewer than 32 rows equals zero-padding it
+ *   qr, sr optional row-wise outputs as mxq_quantize_rowwise (contiguous,
+ *          sr [rows, cols/32]); both NULL or both set
+ *   fq     optional [rows, cols] bf16 = row-wise dequantize(qr, sr) (the
+ *          row-wise codes need not be stored to get it)
+ * Shape: cols % 32 == 0.  Alignment: x, fq 16 bytes; qc, sc, qr 8 bytes.
+ */
+mxq_status mxq_quantize_colwise(const uint16_t *x, int64_t rows, int64_t cols,
+                                uint8_t *qc, uint8_t *sc,
+                                uint8_t *qr, uint8_t *sr, uint16_t *fq, void *stream);
+
+/*
+ * MXFP8 dequantization: out = bf16_RNE(E4M3(q) * 2^(scale - 127)).  NaN code
+ * or scale byte 0xFF gives the quiet NaN 0x7FC0 with the code's sign bit.
+ *   q      [rows, cols] E4M3, contiguous
+ *   scale  axis = 1: [rows, cols/32]; axis = 0: [ceil(rows/32), cols]; contiguous
+ *   out    [rows, cols] bf16, contiguous
+ * Shape: cols % 32 == 0.  Alignment: q 8 bytes, out 16 bytes.
+ */
+mxq_status mxq_dequantize(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
+                          int axis, uint16_t *out, void *stream);
+
+/*
+ * MXFP8 fake quantization (simulated QAT, miles PR #1372 "V4 mxfp4"):
+ * out = dequantize(quantize(x)) along `axis` (1 = row-wise groups, 0 =
+ * column-wise), written as bf16 without materializing the codes.
+ * Shape: cols % 32 == 0.  Contiguous; x and out 16-byte aligned.
+ */
+mxq_status mxq_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, int axis,
+                          uint16_t *out, void *stream);
+
+/*
+ * Grouped row-wise MXFP8: many independent tensors (e.g. every expert of an
+ * MoE layer) in one launch.  Each descriptor is validated as in
+ * mxq_quantize_rowwise (fq is not offered here).
+ */
+typedef struct mxq_group_desc {
+    const uint16_t *x; /* [rows, cols] bf16, row stride ldx */
+    uint8_t *q;        /* [rows, cols] E4M3, row stride ldq */
+    uint8_t *scale;    /* [rows, cols/32] E8M0, row stride lds */
+    int64_t rows, cols, ldx, ldq, lds;
+} mxq_group_desc;
+
+/* Bytes of device workspace mxq_quantize_rowwise_grouped needs for n tensors. */
+size_t mxq_grouped_workspace_size(int32_t n);
+
+/*
+ *   descs      HOST array of n descriptors (read during the call only)
+ *   workspace  DEVICE buffer of >= mxq_grouped_workspace_size(n) bytes,
+ *              16-byte aligned; the library stages a launch table there with
+ *              an async host-to-device copy on `stream`, so the buffer must
+ *              not be reused until the launch has finished
+ * Returns MXQ_EINVAL for n < 0 or NULL pointers, MXQ_ESIZE for a small
+ * workspace, else the first failing descriptor's status.  n == 0 launches
+ * nothing.
+ */
+mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Block-FP8 quantization (xorl PR #30, "What looked solid": block-FP8
+ * absmax): per blk x blk tile, S = fl32(amax / 448), q = E4M3_RNE_sat(fl32(x / S))
+ * with one IEEE fp32 division; an all-zero tile stores S = 0 and codes +-0.
+ * Edge tiles use their valid region.
+ *   x      [rows, cols] bf16, contiguous, 16-byte aligned
+ *   q      [rows, cols] E4M3, contiguous, 8-byte aligned
+ *   scale  [ceil(rows/blk), ceil(cols/blk)] fp32, contiguous
+ * Shape: blk == 128; cols % 8 == 0.
+ */
+mxq_status blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int32_t blk,
+                             uint8_t *q, float *scale, void *stream);
+
+/* Block-FP8 dequantization: out = bf16_RNE(fl32(E4M3(q) * S)); a NaN product
+ * gives the quiet NaN with the code's sign.  Same shapes and rules as above. */
+mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                               int32_t blk, uint16_t *out, void *stream);
+
+/*
+ * NVFP4 two-level quantization (xorl PR #30, "What looked solid":
+ * effective = block_scale * global_scale, clamped, zero block guarded):
+ *   A = max|x| over the tensor; g = fl32(A / 2688)  (2688 = 448 * 6)
+ *   per 16 consecutive values of a row with amax b:
+ *     s = E4M3_RNE_sat(fl32(b / fl32(6 * g))), eff = fl32(E4M3(s) * g)
+ *     q = E2M1_RNE_sat(fl32(x / eff)), or +-0 when eff == 0
+ *   element 2j -> low nibble of byte j, 2j+1 -> high nibble
+ *   x          [rows, cols] bf16, contiguous, 16-byte aligned
+ *   q_packed   [rows, cols/2] bytes, contiguous, 4-byte aligned
+ *   s_e4m3     [rows, cols/16] E4M3 bytes, contiguous
+ *   global_scale  one float (device), written with g
+ *   workspace  >= 4 bytes of device memory, 4-byte aligned, caller-owned,
+ *              used for the tensor-wide amax between two launches
+ * Shape: cols % 16 == 0.
+ */
+mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
+                          uint8_t *s_e4m3, float *global_scale, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* NVFP4 dequantization: out = bf16_RNE(fl32(E2M1(q) * eff)),
+ * eff = fl32(E4M3(s) * g); a NaN product gives the quiet NaN with the
+ * nibble's sign.  Shapes as nvfp4_quantize; out 16-byte aligned. */
+mxq_status nvfp4_dequantize(const uint8_t *q_packed, const uint8_t *s_e4m3,
+                            const float *global_scale, int64_t rows, int64_t cols,
+                            uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

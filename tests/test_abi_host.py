@@ -1,0 +1,168 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+include/mxq.h declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_scaled_precision_mxfp8_amd as mxq
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b((?:mxq|blockfp8|nvfp4)_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mxq.LIB_PATH):
+        pytest.fail("libmxq.so is not built (run __graft_entry__.build())")
+    return mxq.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["mxq_quantize_rowwise", "mxq_quantize_colwise", "mxq_dequantize", "mxq_fake_quant",
+                 "mxq_quantize_rowwise_grouped", "blockfp8_quantize", "blockfp8_dequantize",
+                 "nvfp4_quantize", "nvfp4_dequantize", "mxq_status_string", "mxq_abi_version",
+                 "mxq_grouped_workspace_size"]:
+        assert want in names
+    assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mxq.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_strings(lib):
+    assert lib.mxq_abi_version() == 1
+    for st in range(6):
+        assert lib.mxq_status_string(st)
+    assert b"unknown" in lib.mxq_status_string(99)
+
+
+P16 = ctypes.c_void_p(0x10000)   # aligned fake device addresses: never dereferenced,
+P8 = ctypes.c_void_p(0x10008)    # because every call below fails validation first
+P4 = ctypes.c_void_p(0x10004)
+P2 = ctypes.c_void_p(0x10002)
+NULL = None
+
+
+def test_rowwise_errors(lib):
+    f = lib.mxq_quantize_rowwise
+    assert f(P16, -1, 32, 32, P16, 32, P16, 1, NULL, 0, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 33, 33, P16, 33, P16, 1, NULL, 0, NULL) == mxq.MXQ_ESHAPE
+    assert f(NULL, 4, 32, 32, P16, 32, P16, 1, NULL, 0, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, 32, NULL, 32, P16, 1, NULL, 0, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, 32, P16, 32, NULL, 1, NULL, 0, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 64, 32, P16, 64, P16, 2, NULL, 0, NULL) == mxq.MXQ_ESHAPE   # ldx < cols
+    assert f(P16, 4, 64, 64, P16, 32, P16, 2, NULL, 0, NULL) == mxq.MXQ_ESHAPE   # ldq < cols
+    assert f(P16, 4, 64, 64, P16, 64, P16, 1, NULL, 0, NULL) == mxq.MXQ_ESHAPE   # lds < cols/32
+    assert f(P8, 4, 32, 32, P16, 32, P16, 1, NULL, 0, NULL) == mxq.MXQ_EALIGN    # x not 16-aligned
+    assert f(P16, 4, 32, 36, P16, 32, P16, 1, NULL, 0, NULL) == mxq.MXQ_EALIGN   # ldx % 8
+    assert f(P16, 4, 32, 32, P4, 32, P16, 1, NULL, 0, NULL) == mxq.MXQ_EALIGN    # q not 8-aligned
+    assert f(P16, 4, 32, 32, P16, 36, P16, 1, NULL, 0, NULL) == mxq.MXQ_EALIGN   # ldq % 8
+    assert f(P16, 4, 32, 32, P16, 32, P16, 1, P8, 32, NULL) == mxq.MXQ_EALIGN    # fq not 16-aligned
+    assert f(P16, 4, 32, 32, P16, 32, P16, 1, P16, 16, NULL) == mxq.MXQ_ESHAPE   # ldf < cols
+    assert f(P16, 2**62, 64, 64, P16, 64, P16, 2, NULL, 0, NULL) == mxq.MXQ_ESIZE  # overflow
+    # empty problems are accepted and launch nothing, even with NULL pointers
+    assert f(NULL, 0, 64, 64, NULL, 64, NULL, 2, NULL, 0, NULL) == mxq.MXQ_OK
+    assert f(NULL, 5, 0, 0, NULL, 0, NULL, 0, NULL, 0, NULL) == mxq.MXQ_OK
+
+
+def test_colwise_dequant_fakequant_errors(lib):
+    c = lib.mxq_quantize_colwise
+    assert c(P16, 4, 48, P16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_ESHAPE
+    assert c(P16, 4, 32, NULL, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EINVAL
+    assert c(P16, 4, 32, P16, P16, P16, NULL, NULL, NULL) == mxq.MXQ_EINVAL      # qr without sr
+    assert c(P8, 4, 32, P16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EALIGN
+    assert c(P16, 4, 32, P16, P4, NULL, NULL, NULL, NULL) == mxq.MXQ_EALIGN      # sc 8-aligned
+    assert c(P16, 4, 32, P16, P16, NULL, NULL, P8, NULL) == mxq.MXQ_EALIGN       # fq 16-aligned
+    assert c(NULL, 0, 32, NULL, NULL, NULL, NULL, NULL, NULL) == mxq.MXQ_OK
+    d = lib.mxq_dequantize
+    assert d(P16, P16, 4, 32, 2, P16, NULL) == mxq.MXQ_EINVAL                     # bad axis
+    assert d(P16, P16, 4, 40, 1, P16, NULL) == mxq.MXQ_ESHAPE
+    assert d(P16, NULL, 4, 32, 1, P16, NULL) == mxq.MXQ_EINVAL
+    assert d(P16, P16, 4, 32, 1, P8, NULL) == mxq.MXQ_EALIGN
+    assert d(P16, P4, 4, 32, 0, P16, NULL) == mxq.MXQ_EALIGN
+    fq = lib.mxq_fake_quant
+    assert fq(P16, 4, 32, -1, P16, NULL) == mxq.MXQ_EINVAL
+    assert fq(P16, 4, 31, 1, P16, NULL) == mxq.MXQ_ESHAPE
+    assert fq(P16, 4, 32, 1, NULL, NULL) == mxq.MXQ_EINVAL
+    assert fq(P2, 4, 32, 0, P16, NULL) == mxq.MXQ_EALIGN
+
+
+def test_grouped_errors(lib):
+    g = lib.mxq_quantize_rowwise_grouped
+    assert lib.mxq_grouped_workspace_size(0) == 0
+    ws = lib.mxq_grouped_workspace_size(3)
+    assert ws >= 3 * 64
+    descs = (mxq.GroupDesc * 3)()
+    for i in range(3):
+        descs[i] = mxq.GroupDesc(0x10000, 0x20000, 0x30000, 8, 64, 64, 64, 2)
+    assert g(descs, -1, P16, ws, NULL) == mxq.MXQ_EINVAL
+    assert g(descs, 0, NULL, 0, NULL) == mxq.MXQ_OK
+    assert g(NULL, 3, P16, ws, NULL) == mxq.MXQ_EINVAL
+    assert g(descs, 3, P16, ws - 1, NULL) == mxq.MXQ_ESIZE
+    assert g(descs, 3, P8, ws, NULL) == mxq.MXQ_EALIGN
+    descs[2] = mxq.GroupDesc(0x10000, 0x20000, 0x30000, 8, 48, 48, 48, 2)      # cols % 32
+    assert g(descs, 3, P16, ws, NULL) == mxq.MXQ_ESHAPE
+    descs[2] = mxq.GroupDesc(0x10008, 0x20000, 0x30000, 8, 64, 64, 64, 2)      # x misaligned
+    assert g(descs, 3, P16, ws, NULL) == mxq.MXQ_EALIGN
+    descs[2] = mxq.GroupDesc(0x10000, 0, 0x30000, 8, 64, 64, 64, 2)            # NULL q
+    assert g(descs, 3, P16, ws, NULL) == mxq.MXQ_EINVAL
+
+
+def test_blockfp8_nvfp4_errors(lib):
+    b = lib.blockfp8_quantize
+    assert b(P16, 4, 64, 64, P16, P16, NULL) == mxq.MXQ_ESHAPE                   # blk != 128
+    assert b(P16, 4, 60, 128, P16, P16, NULL) == mxq.MXQ_ESHAPE                  # cols % 8
+    assert b(P16, -4, 64, 128, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert b(P16, 4, 64, 128, NULL, P16, NULL) == mxq.MXQ_EINVAL
+    assert b(P8, 4, 64, 128, P16, P16, NULL) == mxq.MXQ_EALIGN
+    assert b(P16, 4, 64, 128, P16, P2, NULL) == mxq.MXQ_EALIGN
+    bd = lib.blockfp8_dequantize
+    assert bd(P16, P16, 4, 64, 128, P8, NULL) == mxq.MXQ_EALIGN
+    assert bd(P16, NULL, 4, 64, 128, P16, NULL) == mxq.MXQ_EINVAL
+    n = lib.nvfp4_quantize
+    assert n(P16, 4, 24, P16, P16, P16, P16, 4, NULL) == mxq.MXQ_ESHAPE          # cols % 16
+    assert n(P16, 4, 32, P16, P16, P16, NULL, 4, NULL) == mxq.MXQ_EINVAL         # no workspace
+    assert n(P16, 4, 32, P16, P16, P16, P16, 2, NULL) == mxq.MXQ_ESIZE
+    assert n(P8, 4, 32, P16, P16, P16, P16, 4, NULL) == mxq.MXQ_EALIGN
+    assert n(P16, 4, 32, P2, P16, P16, P16, 4, NULL) == mxq.MXQ_EALIGN
+    nd = lib.nvfp4_dequantize
+    assert nd(P16, P16, NULL, 4, 32, P16, NULL) == mxq.MXQ_EINVAL
+    assert nd(P16, P16, P16, 4, 32, P8, NULL) == mxq.MXQ_EALIGN
+    assert nd(NULL, NULL, NULL, 0, 32, NULL, NULL) == mxq.MXQ_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    for fn in (mxq.quantize_rowwise, mxq.fake_quant, mxq.blockfp8_quantize, mxq.nvfp4_quantize,
+               mxq.mxfp8_quantize):
+        with pytest.raises(ValueError):
+            fn(x)
+    with pytest.raises(TypeError):
+        mxq.quantize_rowwise(x.float())
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "block_scaled_precision_mxfp8_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in text.replace("oracle-free", ""), f
