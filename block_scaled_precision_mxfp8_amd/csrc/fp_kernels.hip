@@ -57,6 +57,11 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
     const float div = (m == 0u) ? 1.0f : S;        // zero tile: codes are +-0
     if (tid == 0) scale[bi * tc + bj] = S;
 
+    // Tile-uniform choice: reciprocal + FMA correction (exact for divisors in
+    // [2^-60, 2^60] and |x / S| <= 448 * (1 + 2^-23)), IEEE division
+    // otherwise, all-NaN for a NaN/Inf tile.
+    const bool fast = !nonfinite && markstein_ok(div);
+    const float y = fast ? 1.0f / div : 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int64_t r = rbase + 16 * k;
@@ -65,16 +70,18 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t w0 = w[2 * h], w1 = w[2 * h + 1];
-            const float f[4] = {bf16lo_to_f32(w0), bf16hi_to_f32(w0), bf16lo_to_f32(w1),
-                                bf16hi_to_f32(w1)};
-            uint32_t mags = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float t = __builtin_fabsf(f[j]) / div;   // one IEEE fp32 division
-                mags |= e4m3_mag_from_f32(t) << (8 * j);
+            const float f0 = bf16lo_to_f32(w0), f1 = bf16hi_to_f32(w0);
+            const float f2 = bf16lo_to_f32(w1), f3 = bf16hi_to_f32(w1);
+            if (nonfinite) {
+                c[h] = 0x7F7F7F7Fu | signs4(w0, w1);
+            } else if (fast) {
+                c[h] = cvt_fp8x2_f32<true>(cvt_fp8x2_f32<false>(0u, div_markstein(f0, div, y),
+                                                                div_markstein(f1, div, y)),
+                                           div_markstein(f2, div, y), div_markstein(f3, div, y));
+            } else {
+                c[h] = cvt_fp8x2_f32<true>(cvt_fp8x2_f32<false>(0u, f0 / div, f1 / div),
+                                           f2 / div, f3 / div);   // IEEE fp32 divisions
             }
-            mags = nonfinite ? 0x7F7F7F7Fu : mags;
-            c[h] = mags | signs4(w0, w1);
         }
         if (cin && r < rows) *reinterpret_cast<uint2 *>(q + r * cols + col) = make_uint2(c[0], c[1]);
     }
@@ -109,15 +116,29 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
     const int64_t col = (i - r * cpr) * 8;
     const float S = scale[(r / kBlk) * tc + col / kBlk];
     const uint2 c = *reinterpret_cast<const uint2 *>(q + r * cols + col);
+    const uint32_t tx = c.x & 0x7F7F7F7Fu, ty = c.y & 0x7F7F7F7Fu;
+    const bool nan_code = (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
     uint32_t o[4];
+    if (!wave_any(nan_code || !__builtin_isfinite(S))) {   // NaN products need the sign rule
+        // E4M3 -> fp32 exactly (v_cvt_pk_f32_fp8), one fp32 product, RNE to bf16
+        const uint32_t cw[2] = {c.x, c.y};
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-        const uint32_t cw = j < 4 ? c.x : c.y;
-        const int sh = 8 * (j & 3);
-        const uint32_t c0 = (cw >> sh) & 0xFFu, c1 = (cw >> (sh + 8)) & 0xFFu;
-        const float p0 = e4m3_to_f32(c0) * S;   // one IEEE fp32 multiplication
-        const float p1 = e4m3_to_f32(c1) * S;
-        o[j / 2] = bf16_of_product(p0, c0 & 0x80u) | (bf16_of_product(p1, c1 & 0x80u) << 16);
+        for (int h = 0; h < 2; ++h) {
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[h], false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[h], true);
+            o[2 * h] = bf16x2_rne(a.x * S, a.y * S);
+            o[2 * h + 1] = bf16x2_rne(b.x * S, b.y * S);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            const uint32_t cw = j < 4 ? c.x : c.y;
+            const int sh = 8 * (j & 3);
+            const uint32_t c0 = (cw >> sh) & 0xFFu, c1 = (cw >> (sh + 8)) & 0xFFu;
+            const float p0 = e4m3_to_f32(c0) * S;   // one IEEE fp32 multiplication
+            const float p1 = e4m3_to_f32(c1) * S;
+            o[j / 2] = bf16_of_product(p0, c0 & 0x80u) | (bf16_of_product(p1, c1 & 0x80u) << 16);
+        }
     }
     *reinterpret_cast<uint4 *>(out + r * cols + col) = make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -132,12 +153,15 @@ __global__ void nvfp4_zero_kernel(uint32_t *ws) { ws[0] = 0u; }
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
                                                          int64_t nvec, uint32_t *ws)
 {
+    __shared__ uint32_t red[4];
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride)
         m = max(m, amax8(reinterpret_cast<const uint4 *>(x)[i]));
     m = wave_max(m);
-    if ((threadIdx.x & (kWave - 1)) == 0) atomicMax(ws, m);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(ws, max(max(red[0], red[1]), max(red[2], red[3])));
 }
 
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
@@ -182,21 +206,34 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
         const float eff = e4m3_mag_value(s & 0x7Fu) * g;       // one IEEE fp32 multiplication
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t packed = 0;
+        if (!wave_any(nonfinite || !markstein_ok(eff))) {
+            // reciprocal + FMA correction (exact here), E2M1 by the hardware
+            const float y = 1.0f / eff;
+            packed = cvt_fp4x2_f32<0>(packed, div_markstein(bf16lo_to_f32(w[0]), eff, y),
+                                      div_markstein(bf16hi_to_f32(w[0]), eff, y));
+            packed = cvt_fp4x2_f32<1>(packed, div_markstein(bf16lo_to_f32(w[1]), eff, y),
+                                      div_markstein(bf16hi_to_f32(w[1]), eff, y));
+            packed = cvt_fp4x2_f32<2>(packed, div_markstein(bf16lo_to_f32(w[2]), eff, y),
+                                      div_markstein(bf16hi_to_f32(w[2]), eff, y));
+            packed = cvt_fp4x2_f32<3>(packed, div_markstein(bf16lo_to_f32(w[3]), eff, y),
+                                      div_markstein(bf16hi_to_f32(w[3]), eff, y));
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float f0 = bf16lo_to_f32(w[j]), f1 = bf16hi_to_f32(w[j]);
-            uint32_t n0, n1;
-            if (nonfinite) {
-                n0 = n1 = 7u;
-            } else if (eff == 0.0f) {
-                n0 = n1 = 0u;
-            } else {
-                n0 = e2m1_mag_from_f32(__builtin_fabsf(f0) / eff);   // one IEEE fp32 division
-                n1 = e2m1_mag_from_f32(__builtin_fabsf(f1) / eff);
+            for (int j = 0; j < 4; ++j) {
+                const float f0 = bf16lo_to_f32(w[j]), f1 = bf16hi_to_f32(w[j]);
+                uint32_t n0, n1;
+                if (nonfinite) {
+                    n0 = n1 = 7u;
+                } else if (eff == 0.0f) {
+                    n0 = n1 = 0u;
+                } else {
+                    n0 = e2m1_mag_from_f32(__builtin_fabsf(f0) / eff);   // one IEEE fp32 division
+                    n1 = e2m1_mag_from_f32(__builtin_fabsf(f1) / eff);
+                }
+                n0 |= (w[j] >> 12) & 0x8u;          // sign of the low bf16
+                n1 |= (w[j] >> 28) & 0x8u;          // sign of the high bf16
+                packed |= (n0 | (n1 << 4)) << (8 * j);
             }
-            n0 |= (w[j] >> 12) & 0x8u;          // sign of the low bf16
-            n1 |= (w[j] >> 28) & 0x8u;          // sign of the high bf16
-            packed |= (n0 | (n1 << 4)) << (8 * j);
         }
         if (ok) {
             *reinterpret_cast<uint32_t *>(q + r * (cols >> 1) + (col >> 1)) = packed;
@@ -222,15 +259,27 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__res
     const float eff = e4m3_to_f32(sb) * g;                 // one IEEE fp32 multiplication
     const uint32_t packed = *reinterpret_cast<const uint32_t *>(q + r * (cols >> 1) + (col >> 1));
     uint32_t o[4];
+    if (!wave_any(!__builtin_isfinite(eff))) {   // NaN products (x * NaN, 0 * Inf) need the sign rule
+        // E2M1 -> fp32 exactly (v_cvt_scalef32_pk_f32_fp4, scale 1), one product, RNE
+        const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
+        const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 1);
+        const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 2);
+        const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 3);
+        o[0] = bf16x2_rne(p0.x * eff, p0.y * eff);
+        o[1] = bf16x2_rne(p1.x * eff, p1.y * eff);
+        o[2] = bf16x2_rne(p2.x * eff, p2.y * eff);
+        o[3] = bf16x2_rne(p3.x * eff, p3.y * eff);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t byte = (packed >> (8 * j)) & 0xFFu;
-        const uint32_t n0 = byte & 0xFu, n1 = byte >> 4;
-        float v0 = e2m1_mag_value(n0 & 7u), v1 = e2m1_mag_value(n1 & 7u);
-        v0 = (n0 & 8u) ? -v0 : v0;
-        v1 = (n1 & 8u) ? -v1 : v1;
-        const float p0 = v0 * eff, p1 = v1 * eff;         // one IEEE fp32 multiplication each
-        o[j] = bf16_of_product(p0, n0 & 8u) | (bf16_of_product(p1, n1 & 8u) << 16);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t byte = (packed >> (8 * j)) & 0xFFu;
+            const uint32_t n0 = byte & 0xFu, n1 = byte >> 4;
+            float v0 = e2m1_mag_value(n0 & 7u), v1 = e2m1_mag_value(n1 & 7u);
+            v0 = (n0 & 8u) ? -v0 : v0;
+            v1 = (n1 & 8u) ? -v1 : v1;
+            const float q0 = v0 * eff, q1 = v1 * eff;       // one IEEE fp32 multiplication each
+            o[j] = bf16_of_product(q0, n0 & 8u) | (bf16_of_product(q1, n1 & 8u) << 16);
+        }
     }
     *reinterpret_cast<uint4 *>(out + r * cols + col) = make_uint4(o[0], o[1], o[2], o[3]);
 }
@@ -272,7 +321,7 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t want = (nvec + 255) / 256;
-    const int64_t ablocks = want < 4096 ? want : 4096;
+    const int64_t ablocks = want < 1024 ? want : 1024;   // one atomic per workgroup
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -28,18 +28,20 @@ constexpr int kColTileRows = 128;  // rows per column-wise workgroup tile (4 wav
 
 // ---------------------------------------------------------------------------
 // Row-wise tile: rows [rb*32, rb*32+32) x columns of segment `seg`.
+// kFull: the whole tile is inside the tensor (wave-uniform), so no load or
+// store needs a predicate.
 // ---------------------------------------------------------------------------
-template <bool kQ, bool kFQ>
-__device__ __forceinline__ void mx_row_tile(const uint16_t *__restrict__ x, int64_t rows,
-                                            int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
-                                            int64_t ldq, uint8_t *__restrict__ scale, int64_t lds,
-                                            uint16_t *__restrict__ fq, int64_t ldf, int64_t seg,
-                                            int64_t rb)
+template <bool kQ, bool kFQ, bool kFull>
+__device__ __forceinline__ void mx_row_tile_impl(const uint16_t *__restrict__ x, int64_t rows,
+                                                 int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
+                                                 int64_t ldq, uint8_t *__restrict__ scale,
+                                                 int64_t lds, uint16_t *__restrict__ fq, int64_t ldf,
+                                                 int64_t seg, int64_t rb)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSeg + lane * 8;
-    const bool cin = col < cols;  // cols % 32 == 0: a quad is all in or all out
+    const bool cin = kFull || col < cols;  // cols % 32 == 0: a quad is all in or all out
     const int64_t r0 = rb * kRowsPerTile + wave;
 
 #pragma unroll
@@ -49,29 +51,55 @@ __device__ __forceinline__ void mx_row_tile(const uint16_t *__restrict__ x, int6
         for (int u = 0; u < kU; ++u) {
             const int64_t r = r0 + 4 * (it * kU + u);
             v[u] = make_uint4(0, 0, 0, 0);
-            if (cin && r < rows) v[u] = *reinterpret_cast<const uint4 *>(x + r * ldx + col);
+            if (kFull || (cin && r < rows)) v[u] = *reinterpret_cast<const uint4 *>(x + r * ldx + col);
         }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t r = r0 + 4 * (it * kU + u);
-            const bool ok = cin && r < rows;
+            const bool ok = kFull || (cin && r < rows);
             const uint32_t s = mx_scale_byte(quad_max(amax8(v[u])));
             const bool nan_group = s == 0xFFu;
-            const int e = 7 - (int)s;
-            const uint32_t c0 = e4m3x4_row(v[u].x, v[u].y, e, nan_group);
-            const uint32_t c1 = e4m3x4_row(v[u].z, v[u].w, e, nan_group);
+            const uint32_t lim = mx_limit_bf16(s);
+            const uint32_t lim2 = lim | (lim << 16);
+            const float sf = e8m0_to_f32(s);
+            uint32_t c0 = e4m3x4_row_hw(v[u].x, v[u].y, lim2, sf);
+            uint32_t c1 = e4m3x4_row_hw(v[u].z, v[u].w, lim2, sf);
+            if (nan_group) {
+                c0 = 0x7F7F7F7Fu | signs4(v[u].x, v[u].y);
+                c1 = 0x7F7F7F7Fu | signs4(v[u].z, v[u].w);
+            }
             if (kQ && ok) {
                 *reinterpret_cast<uint2 *>(q + r * ldq + col) = make_uint2(c0, c1);
-                if ((lane & 3) == 0) scale[r * lds + (col >> 5)] = (uint8_t)s;
+                // all 4 lanes of the quad hold the same byte: storing it from
+                // each avoids an exec-mask change per row
+                scale[r * lds + (col >> 5)] = (uint8_t)s;
             }
             if (kFQ) {
-                const int edq = (int)s - 7;
-                const uint2 lo = mx_dequant4(c0, edq, nan_group);
-                const uint2 hi = mx_dequant4(c1, edq, nan_group);
+                uint2 lo, hi;
+                if (wave_any(nan_group)) {   // rare: a NaN/Inf group in this row of the wave
+                    lo = mx_dequant4(c0, (int)s - 7, nan_group);
+                    hi = mx_dequant4(c1, (int)s - 7, nan_group);
+                } else {
+                    lo = mx_dequant4_hw(c0, sf);
+                    hi = mx_dequant4_hw(c1, sf);
+                }
                 if (ok) *reinterpret_cast<uint4 *>(fq + r * ldf + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
         }
     }
+}
+
+template <bool kQ, bool kFQ>
+__device__ __forceinline__ void mx_row_tile(const uint16_t *__restrict__ x, int64_t rows,
+                                            int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
+                                            int64_t ldq, uint8_t *__restrict__ scale, int64_t lds,
+                                            uint16_t *__restrict__ fq, int64_t ldf, int64_t seg,
+                                            int64_t rb)
+{
+    if ((seg + 1) * kSeg <= cols && (rb + 1) * kRowsPerTile <= rows)
+        mx_row_tile_impl<kQ, kFQ, true>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, seg, rb);
+    else
+        mx_row_tile_impl<kQ, kFQ, false>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, seg, rb);
 }
 
 template <bool kQ, bool kFQ>
@@ -90,7 +118,152 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
 // Column-wise (+ row-wise + fake-quant) in one read of x.  A wave holds one
 // 32-row group x 512 columns in registers (32 x 16 bytes per lane): the column
 // amax is an in-lane max over the 32 loads, the row amax a quad max per row.
+// Column codes go through the hardware convert two rows at a time (the pair
+// it converts must share one scale, i.e. one column).
 // ---------------------------------------------------------------------------
+template <bool kCol, bool kRow, bool kFQRow, bool kFQCol, bool kFull>
+__device__ __forceinline__ void mx_colwise_body(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qc,
+    uint8_t *__restrict__ sc, uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
+    uint16_t *__restrict__ fq_row, uint16_t *__restrict__ fq_col, int64_t g, int64_t col)
+{
+    constexpr bool kColAny = kCol || kFQCol;
+    constexpr bool kRowAny = kRow || kFQRow;
+    const bool cin = kFull || col < cols;
+    const int64_t r0 = g * 32;
+    const int64_t ngr = cols >> 5;
+
+    uint4 v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (kFull || (cin && r0 + i < rows))
+            v[i] = *reinterpret_cast<const uint4 *>(x + (r0 + i) * cols + col);
+    }
+
+    // column scales: in-lane amax over the 32 rows, one E8M0 byte per column
+    uint32_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    bool nan[8] = {false, false, false, false, false, false, false, false};
+    bool col_slow = false;
+    uint32_t lim2[4] = {0, 0, 0, 0};
+    float sf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (kColAny) {
+        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            m0 = pk_max_u16(m0, mag2(v[i].x));
+            m1 = pk_max_u16(m1, mag2(v[i].y));
+            m2 = pk_max_u16(m2, mag2(v[i].z));
+            m3 = pk_max_u16(m3, mag2(v[i].w));
+        }
+        const uint32_t am[8] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16,
+                                m2 & 0xFFFFu, m2 >> 16, m3 & 0xFFFFu, m3 >> 16};
+        bool any_nan = false;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            s[j] = mx_scale_byte(am[j]);
+            nan[j] = s[j] == 0xFFu;
+            any_nan |= nan[j];
+            sf[j] = e8m0_to_f32(s[j]);
+            e[j] = 7 - (int)s[j];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            lim2[k] = mx_limit_bf16(s[2 * k]) | (mx_limit_bf16(s[2 * k + 1]) << 16);
+        if (kCol && cin) {
+            const uint32_t lo = s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24);
+            const uint32_t hi = s[4] | (s[5] << 8) | (s[6] << 16) | (s[7] << 24);
+            *reinterpret_cast<uint2 *>(sc + g * cols + col) = make_uint2(lo, hi);
+        }
+        col_slow = wave_any(any_nan);  // a NaN/Inf column in the wave: exact software path
+    }
+
+    // one row of column codes (and its column-wise fake-quant) out
+    auto put_col_row = [&](int i, uint32_t c0, uint32_t c1) __attribute__((always_inline)) {
+        const int64_t r = r0 + i;
+        const bool ok = kFull || (cin && r < rows);
+        if (kCol && ok) *reinterpret_cast<uint2 *>(qc + r * cols + col) = make_uint2(c0, c1);
+        if (kFQCol) {
+            uint32_t bb[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bb[j] = mx_dequant1((c0 >> (8 * j)) & 0xFFu, (int)s[j] - 7, nan[j]);
+                bb[4 + j] = mx_dequant1((c1 >> (8 * j)) & 0xFFu, (int)s[4 + j] - 7, nan[4 + j]);
+            }
+            if (ok)
+                *reinterpret_cast<uint4 *>(fq_col + r * cols + col) =
+                    make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16),
+                               bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16));
+        }
+    };
+
+    // one row's row-wise codes, scale byte and fake-quant out
+    auto row_work = [&](int i) __attribute__((always_inline)) {
+        const int64_t r = r0 + i;
+        const bool ok = kFull || (cin && r < rows);
+        const uint32_t sr_b = mx_scale_byte(quad_max(amax8(v[i])));
+        const bool nan_group = sr_b == 0xFFu;
+        const uint32_t lim = mx_limit_bf16(sr_b);
+        const uint32_t l2 = lim | (lim << 16);
+        const float sfr = e8m0_to_f32(sr_b);
+        uint32_t c0 = e4m3x4_row_hw(v[i].x, v[i].y, l2, sfr);
+        uint32_t c1 = e4m3x4_row_hw(v[i].z, v[i].w, l2, sfr);
+        if (nan_group) {
+            c0 = 0x7F7F7F7Fu | signs4(v[i].x, v[i].y);
+            c1 = 0x7F7F7F7Fu | signs4(v[i].z, v[i].w);
+        }
+        if (kRow && ok) {
+            *reinterpret_cast<uint2 *>(qr + r * cols + col) = make_uint2(c0, c1);
+            sr[r * ngr + (col >> 5)] = (uint8_t)sr_b;  // same byte from the 4 lanes of a quad
+        }
+        if (kFQRow) {
+            uint2 lo, hi;
+            if (wave_any(nan_group)) {  // rare: a NaN/Inf group in this row of the wave
+                lo = mx_dequant4(c0, (int)sr_b - 7, nan_group);
+                hi = mx_dequant4(c1, (int)sr_b - 7, nan_group);
+            } else {
+                lo = mx_dequant4_hw(c0, sfr);
+                hi = mx_dequant4_hw(c1, sfr);
+            }
+            if (ok)
+                *reinterpret_cast<uint4 *>(fq_row + r * cols + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+    };
+
+    static_for<0, 32, 2>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if (kColAny) {
+            if (!col_slow) {
+                // the pair fed to one convert shares a scale: same column, rows i and i+1
+                const uint32_t a[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                const uint32_t b[4] = {v[i + 1].x, v[i + 1].y, v[i + 1].z, v[i + 1].w};
+                uint32_t rp[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    rp[k] = e4m3_colpair_hw(clamp_mag2(a[k], lim2[k]), clamp_mag2(b[k], lim2[k]),
+                                            sf[2 * k], sf[2 * k + 1]);
+                put_col_row(i, __builtin_amdgcn_perm(rp[1], rp[0], 0x06040200u),
+                            __builtin_amdgcn_perm(rp[3], rp[2], 0x06040200u));
+                put_col_row(i + 1, __builtin_amdgcn_perm(rp[1], rp[0], 0x07050301u),
+                            __builtin_amdgcn_perm(rp[3], rp[2], 0x07050301u));
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    put_col_row(i + h,
+                                e4m3x4_col(v[i + h].x, v[i + h].y, e[0], e[1], e[2], e[3], nan[0],
+                                           nan[1], nan[2], nan[3]),
+                                e4m3x4_col(v[i + h].z, v[i + h].w, e[4], e[5], e[6], e[7], nan[4],
+                                           nan[5], nan[6], nan[7]));
+            }
+        }
+        if (kRowAny) {
+            row_work(i);
+            row_work(i + 1);
+        }
+    });
+}
+
 template <bool kCol, bool kRow, bool kFQRow, bool kFQCol>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mx_colwise_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qc,
@@ -103,90 +276,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSeg + lane * 8;
-    const bool cin = col < cols;
     const int64_t g = rb * (kColTileRows / 32) + wave;  // 32-row group index
-    const int64_t r0 = g * 32;
-    if (r0 >= rows) return;  // wave-uniform; the kernel has no barriers
-
-    uint4 v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (cin && r0 + i < rows) v[i] = *reinterpret_cast<const uint4 *>(x + (r0 + i) * cols + col);
-    }
-
-    if (kCol || kFQCol) {
-        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            m0 = pk_max_u16(m0, mag2(v[i].x));
-            m1 = pk_max_u16(m1, mag2(v[i].y));
-            m2 = pk_max_u16(m2, mag2(v[i].z));
-            m3 = pk_max_u16(m3, mag2(v[i].w));
-        }
-        const uint32_t am[8] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16,
-                                m2 & 0xFFFFu, m2 >> 16, m3 & 0xFFFFu, m3 >> 16};
-        uint32_t s[8];
-        int e[8], edq[8];
-        bool nan[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            s[j] = mx_scale_byte(am[j]);
-            nan[j] = s[j] == 0xFFu;
-            e[j] = 7 - (int)s[j];
-            edq[j] = (int)s[j] - 7;
-        }
-        if (kCol && cin) {
-            const uint32_t lo = s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24);
-            const uint32_t hi = s[4] | (s[5] << 8) | (s[6] << 16) | (s[7] << 24);
-            *reinterpret_cast<uint2 *>(sc + g * cols + col) = make_uint2(lo, hi);
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int64_t r = r0 + i;
-            const bool ok = cin && r < rows;
-            const uint32_t c0 = e4m3x4_col(v[i].x, v[i].y, e, nan);
-            const uint32_t c1 = e4m3x4_col(v[i].z, v[i].w, e + 4, nan + 4);
-            if (kCol && ok) *reinterpret_cast<uint2 *>(qc + r * cols + col) = make_uint2(c0, c1);
-            if (kFQCol) {
-                uint32_t b[8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    b[j] = mx_dequant1((c0 >> (8 * j)) & 0xFFu, edq[j], nan[j]);
-                    b[4 + j] = mx_dequant1((c1 >> (8 * j)) & 0xFFu, edq[4 + j], nan[4 + j]);
-                }
-                if (ok)
-                    *reinterpret_cast<uint4 *>(fq_col + r * cols + col) =
-                        make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
-                                   b[6] | (b[7] << 16));
-            }
-        }
-    }
-
-    if (kRow || kFQRow) {
-        const int64_t ngr = cols >> 5;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int64_t r = r0 + i;
-            const bool ok = cin && r < rows;
-            const uint32_t s = mx_scale_byte(quad_max(amax8(v[i])));
-            const bool nan_group = s == 0xFFu;
-            const int e = 7 - (int)s;
-            const uint32_t c0 = e4m3x4_row(v[i].x, v[i].y, e, nan_group);
-            const uint32_t c1 = e4m3x4_row(v[i].z, v[i].w, e, nan_group);
-            if (kRow && ok) {
-                *reinterpret_cast<uint2 *>(qr + r * cols + col) = make_uint2(c0, c1);
-                if ((lane & 3) == 0) sr[r * ngr + (col >> 5)] = (uint8_t)s;
-            }
-            if (kFQRow) {
-                const int edq = (int)s - 7;
-                const uint2 lo = mx_dequant4(c0, edq, nan_group);
-                const uint2 hi = mx_dequant4(c1, edq, nan_group);
-                if (ok)
-                    *reinterpret_cast<uint4 *>(fq_row + r * cols + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-        }
-    }
+    if (g * 32 >= rows) return;  // wave-uniform; the kernel has no barriers
+    if ((seg + 1) * kSeg <= cols && g * 32 + 32 <= rows)
+        mx_colwise_body<kCol, kRow, kFQRow, kFQCol, true>(x, rows, cols, qc, sc, qr, sr, fq_row,
+                                                          fq_col, g, col);
+    else
+        mx_colwise_body<kCol, kRow, kFQRow, kFQCol, false>(x, rows, cols, qc, sc, qr, sr, fq_row,
+                                                           fq_col, g, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -216,8 +313,18 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
         if (kAxis == 1) {
             const uint32_t s = scale[r * (cols >> 5) + (col >> 5)];
             const bool nan = s == 0xFFu;
-            const uint2 lo = mx_dequant4(c.x, (int)s - 7, nan);
-            const uint2 hi = mx_dequant4(c.y, (int)s - 7, nan);
+            // a byte of the form S.1111.111 (NaN code) in either word?
+            const uint32_t tx = c.x & 0x7F7F7F7Fu, ty = c.y & 0x7F7F7F7Fu;
+            const bool nan_code = (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
+            uint2 lo, hi;
+            if (wave_any(nan || nan_code)) {
+                lo = mx_dequant4(c.x, (int)s - 7, nan);
+                hi = mx_dequant4(c.y, (int)s - 7, nan);
+            } else {
+                const float sf = e8m0_to_f32(s);
+                lo = mx_dequant4_hw(c.x, sf);
+                hi = mx_dequant4_hw(c.y, sf);
+            }
             b[0] = lo.x; b[1] = lo.y; b[2] = hi.x; b[3] = hi.y;
         } else {
             const uint2 sv = *reinterpret_cast<const uint2 *>(scale + (r >> 5) * cols + col);

@@ -15,7 +15,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mxq {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B, B+S, ... < E.
+// Keeps register-array indices static where a #pragma unroll could give up on
+// a large body (and fall back to scratch memory for the array).
+template <int B, int E, int S, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + S, E, S>(f);
+    }
+}
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -130,13 +144,13 @@ __device__ __forceinline__ uint32_t e4m3x4_row(uint32_t w0, uint32_t w1, int e, 
 }
 
 // Same with a separate exponent / NaN flag per element (column groups).
-__device__ __forceinline__ uint32_t e4m3x4_col(uint32_t w0, uint32_t w1, const int e[4],
-                                               const bool nan[4])
+__device__ __forceinline__ uint32_t e4m3x4_col(uint32_t w0, uint32_t w1, int e0, int e1, int e2,
+                                               int e3, bool n0, bool n1, bool n2, bool n3)
 {
-    uint32_t c0 = nan[0] ? 0x7Fu : e4m3_mag_bf16hi(w0 << 16, e[0]);
-    uint32_t c1 = nan[1] ? 0x7Fu : e4m3_mag_bf16hi(w0 & 0xFFFF0000u, e[1]);
-    uint32_t c2 = nan[2] ? 0x7Fu : e4m3_mag_bf16hi(w1 << 16, e[2]);
-    uint32_t c3 = nan[3] ? 0x7Fu : e4m3_mag_bf16hi(w1 & 0xFFFF0000u, e[3]);
+    uint32_t c0 = n0 ? 0x7Fu : e4m3_mag_bf16hi(w0 << 16, e0);
+    uint32_t c1 = n1 ? 0x7Fu : e4m3_mag_bf16hi(w0 & 0xFFFF0000u, e1);
+    uint32_t c2 = n2 ? 0x7Fu : e4m3_mag_bf16hi(w1 << 16, e2);
+    uint32_t c3 = n3 ? 0x7Fu : e4m3_mag_bf16hi(w1 & 0xFFFF0000u, e3);
     return (c0 | (c1 << 8) | (c2 << 16) | (c3 << 24)) | signs4(w0, w1);
 }
 
@@ -150,6 +164,18 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
 {
     uint32_t u = __float_as_uint(f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 (finite or Inf) -> packed bf16 (a in the low half), RNE on the bit
+// patterns; the sign rides along and overflow carries into Inf.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b)
+{
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    ua += 0x7FFFu + ((ua >> 16) & 1u);
+    ub += 0x7FFFu + ((ub >> 16) & 1u);
+    return __builtin_amdgcn_perm(ub, ua, 0x07060302u);
 }
 
 // E4M3 magnitude code (0..0x7E) as fp32: the rebias trick in reverse.
@@ -215,6 +241,132 @@ __device__ __forceinline__ float e2m1_mag_value(uint32_t mag)
 {
     return __builtin_amdgcn_ldexpf(__uint_as_float(mag << 22), 126);
 }
+
+// ---------------------------------------------------------------------------
+// Hardware-assisted MX encode / decode (gfx950 scaled converts).
+//
+// v_cvt_scalef32_pk_fp8_bf16 converts two bf16 to E4M3 as RNE(x / scale).
+// Run over every bf16 pattern and 17 power-of-two scales from 2^-127 to
+// 2^127 on MI355X, it returned exactly the reference encoding for every
+// |x / scale| <= 464, including E4M3 subnormals, signed zeros and bf16
+// subnormal inputs; above that it returns the NaN code instead of
+// saturating.  Clamping each magnitude to 448 * scale first (exact: a bf16
+// value) therefore makes it the saturating RNE encoder of the method.
+// ---------------------------------------------------------------------------
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// bf16 bits of 448 * 2^(s - 127) (exponent field s + 8, fraction 0.75).
+__device__ __forceinline__ uint32_t mx_limit_bf16(uint32_t s) { return ((s + 8u) << 7) | 0x60u; }
+
+// 2^(s - 127) as fp32 (s <= 254; s = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
+{
+    return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+// Clamp both bf16 magnitudes of w to the packed limit lim2, keeping signs.
+__device__ __forceinline__ uint32_t clamp_mag2(uint32_t w, uint32_t lim2)
+{
+    return (w & 0x80008000u) | pk_min_u16(w & 0x7FFF7FFFu, lim2);
+}
+
+// Two E4M3 codes of the (already clamped) bf16 pair w into half `kHi` of old.
+template <bool kHi>
+__device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t old, uint32_t w, float scale)
+{
+    const i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(
+        __builtin_bit_cast(i16x2, old), __builtin_bit_cast(bf16x2, w), scale, kHi);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 4 codes of one row group (finite scale byte s): bytes 0..3 <- (w0.lo, w0.hi, w1.lo, w1.hi).
+__device__ __forceinline__ uint32_t e4m3x4_row_hw(uint32_t w0, uint32_t w1, uint32_t lim2,
+                                                  float scale)
+{
+    return cvt_fp8x2<true>(cvt_fp8x2<false>(0u, clamp_mag2(w0, lim2), scale),
+                           clamp_mag2(w1, lim2), scale);
+}
+
+// Column groups: the pair fed to one convert must share a scale, so it is
+// made of the same column in two consecutive rows.  For dword k (columns 2k,
+// 2k+1) of rows i and i+1 (already clamped): returns bytes
+// [(i,2k), (i+1,2k), (i,2k+1), (i+1,2k+1)].
+__device__ __forceinline__ uint32_t e4m3_colpair_hw(uint32_t a, uint32_t b, float s_lo, float s_hi)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo, b.lo)
+    const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi, b.hi)
+    return cvt_fp8x2<true>(cvt_fp8x2<false>(0u, lo, s_lo), hi, s_hi);
+}
+
+// MX dequantization with v_cvt_scalef32_pk_bf16_fp8 (E4M3 * scale -> bf16).
+// Over all 256 codes x every E8M0 scale 2^-127..2^127 on MI355X it matched
+// the reference bit for bit -- bf16 subnormal results and overflow to Inf
+// included -- except the NaN codes, which it turns into 0xFFC0 whatever
+// their sign; callers route groups that can hold NaN to mx_dequant4.
+__device__ __forceinline__ uint2 mx_dequant4_hw(uint32_t c, float scale)
+{
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// ---------------------------------------------------------------------------
+// fp32 quotients and fp32 -> E4M3 / E2M1 with the hardware converts
+// ---------------------------------------------------------------------------
+
+// x / d for d > 0 from y = RN(1/d) with two FMAs (Markstein's correction
+// step), the sign taken from x (the correction alone turns -0 into +0).
+// Checked on the host against IEEE division: for every bf16 significand of x,
+// every fp32 significand of d and five quotient binades the results are
+// identical (5.4e9 cases); over every bf16 x (zeros, subnormals, both signs)
+// with |x| <= 512 d, d at 2^-60, 2^-30, 1, 2^30 and 2^59 times every 61st
+// significand (2.4e10 cases) they are identical except for quotients below
+// 2^-30, where both stay below 2^-30 with the same sign -- far under every
+// rounding threshold of E4M3 and E2M1.  Callers therefore use it only for d
+// in [2^-60, 2^60] and quotients of magnitude <= 512.
+__device__ __forceinline__ float div_markstein(float x, float d, float y)
+{
+    const float q0 = x * y;
+    const float r = __builtin_fmaf(-q0, d, x);
+    return __builtin_copysignf(__builtin_fmaf(r, y, q0), x);
+}
+
+__device__ __forceinline__ bool markstein_ok(float d)
+{
+    return d >= 0x1p-60f && d <= 0x1p60f;
+}
+
+// Two fp32 -> E4M3 codes (RNE, saturating) into half kHi of old.
+// v_cvt_pk_fp8_f32 matched the reference for every |t| <= 448 tried on
+// MI355X (all bf16 patterns and 65,536 random full-precision fp32 values);
+// above 448 it gives the NaN code, hence the clamp.
+template <bool kHi>
+__device__ __forceinline__ uint32_t cvt_fp8x2_f32(uint32_t old, float a, float b)
+{
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
+}
+
+// Two fp32 -> E2M1 nibbles (RNE, saturating at +-6; lo nibble <- a) into byte
+// kByte of old.  v_cvt_scalef32_pk_fp4_f32 with scale 1 matched the reference
+// on all bf16 patterns and 65,536 random fp32 values, saturation included.
+template <int kByte>
+__device__ __forceinline__ uint32_t cvt_fp4x2_f32(uint32_t old, float a, float b)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, kByte);
+}
+
+// Wave-uniform OR of a lane predicate.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 // bf16 bits in the low half of u -> fp32 value.
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t u) { return __uint_as_float(u << 16); }

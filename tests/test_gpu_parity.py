@@ -200,6 +200,18 @@ def test_dequant_all_codes_all_scales(gpu, orc, axis):
     assert_same(f"dequant axis {axis}", bits16(out), orc.mxfp8_dequantize(q, s, axis))
 
 
+def test_dequant_hw_path_all_finite_pairs(gpu, orc):
+    """Every non-NaN E4M3 code x every finite scale byte, laid out so no wave
+    sees a NaN code or a NaN scale (the hardware-decode path)."""
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F] + [0, 0], dtype=np.uint8)
+    q = np.tile(finite, (255, 1))                                  # [255, 256]
+    s = np.repeat(np.arange(255, dtype=np.uint8)[:, None], 8, axis=1)
+    announce("dequant hw path")
+    out = gpu.dequantize(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), axis=1)
+    torch.cuda.synchronize()
+    assert_same("dequant hw path", bits16(out), orc.mxfp8_dequantize(q, s, 1))
+
+
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("shape", [(256, 512), (33, 64), (100, 7168)])
 def test_fake_quant(gpu, orc, axis, shape):
@@ -287,6 +299,29 @@ def test_blockfp8_nonfinite_and_tiny_tiles(gpu, orc):
     check_blockfp8(gpu, orc, xb, "b-edge")
 
 
+def bf16_of(v):
+    return workloads.bf16_from_float(v)
+
+
+def test_blockfp8_division_paths(gpu, orc):
+    """Tiles on both sides of the reciprocal-division domain (scale in
+    [2^-60, 2^60]) and signed zeros in each."""
+    xb = workloads.random_bf16((128, 128 * 6), 72)
+    amax = [2.0 ** -52, 2.0 ** -51, 1.0, 2.0 ** 68.5, 2.0 ** 69, 2.0 ** 120]  # S = amax/448
+    for t, a in enumerate(amax):
+        tile = xb[:, 128 * t:128 * (t + 1)].astype(np.int64)
+        scale = a / 4.0
+        vals = workloads.random_bf16((128, 128), 80 + t)
+        tile[:] = workloads.bf16_bits((torch.from_numpy(vals.view(np.int16)).view(torch.bfloat16)
+                                       .float().numpy() * scale).astype(np.float32))
+        tile[5, 5] = bf16_of(a)
+        tile[6, 6] = 0x8000                                         # -0
+        tile[7, 7] = 0x0000
+        tile[8, 8] = 0x8001                                         # -min subnormal
+        xb[:, 128 * t:128 * (t + 1)] = tile
+    check_blockfp8(gpu, orc, np.ascontiguousarray(xb), "b-divpaths")
+
+
 def test_blockfp8_square_8192_full(gpu, orc):
     check_blockfp8(gpu, orc, workloads.square_8192(), "square_8192")
 
@@ -321,6 +356,20 @@ def test_nvfp4_degenerate(gpu, orc):
     big = workloads.random_bf16((16, 64), 6)
     big[0, 0] = 0x7F7F                                      # max finite bf16
     check_nvfp4(gpu, orc, big, "max")
+
+
+@pytest.mark.parametrize("amax", [2.0 ** -48, 2.0 ** -40, 1.0, 2.0 ** 60, 2.0 ** 70])
+def test_nvfp4_division_paths(gpu, orc, amax):
+    """Global scales that put block effective scales on both sides of the
+    reciprocal-division domain; signed zeros; zero blocks beside tiny ones."""
+    x = workloads.random_bf16((64, 256), 90)
+    xf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float().numpy() * (amax / 8.0)
+    xb = workloads.bf16_bits(xf.astype(np.float32))
+    xb[0, 0] = bf16_of(amax)
+    xb[1, :16] = 0                                                  # a zero block
+    xb[2, 3] = 0x8000                                               # -0
+    xb[3, 16:32] = 0x0001                                           # subnormal block
+    check_nvfp4(gpu, orc, xb, f"n-divpaths-{amax:g}")
 
 
 def test_nvfp4_square_8192_full(gpu, orc):
