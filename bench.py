@@ -146,22 +146,27 @@ def main():
     ms_per_step = ms_total / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # per-launch durations of the kernel (one launch per step), HIP events
-    durs = []
-    for _ in range(max(10, min(args.steps, 50))):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+    # The step is exactly one launch of the one-pass kernel on `stream`, so the
+    # HIP-event average over the timed region is the kernel's average launch
+    # duration.  Per-launch spread: events recorded between back-to-back
+    # launches (each interval also holds one event's own overhead).
+    kern_ms = ms_per_step
+    nl = max(10, min(args.steps, 50))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(nl):
         step()
-        b.record(stream)
-        b.synchronize()
-        durs.append(a.elapsed_time(b))
-    kern_ms = statistics.mean(durs)
+        evs[i + 1].record(stream)
+    evs[-1].synchronize()
+    durs = [evs[i].elapsed_time(evs[i + 1]) for i in range(nl)]
     achieved = step_bytes / (kern_ms * 1e-3) / 1e9
     traffic = read_traffic("act_16384")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "mx_colwise_kernel<col,row,fq>", "algorithmic_bytes": step_bytes,
-                "avg_launch_us": round(kern_ms * 1e3, 2)}
+                "avg_launch_us": round(kern_ms * 1e3, 2),
+                "per_launch_us_min_max": [round(min(durs) * 1e3, 2), round(max(durs) * 1e3, 2)]}
     log(f"main: {value:.1f} GB/s per step, kernel {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
 
     # plain device copy of the same byte count: the practical ceiling
@@ -206,7 +211,10 @@ def main():
     # ------------------------------------------------------------------
     breakdown = {}
     if not args.no_breakdown:
-        flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        # Inputs under 256 MB would sit in the Infinity Cache between repeats:
+        # before each timed launch, read 1 GiB (a read leaves no dirty lines
+        # whose write-back would land in the timed kernel).
+        flush = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
 
         def timed(fn, nbytes, iters=20, flush_cache=True):
             for _ in range(3):
@@ -214,7 +222,7 @@ def main():
             ts = []
             for _ in range(iters):
                 if flush_cache:
-                    flush.zero_()
+                    flush.max()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
                 fn()

@@ -20,6 +20,7 @@ namespace mxq {
 constexpr int kBlk = 128;   // block-FP8 tile edge
 constexpr int kSegNv = 512; // NVFP4 columns per wave segment (64 lanes x 8)
 constexpr int kRowsNv = 32; // NVFP4 rows per workgroup tile
+constexpr bool kNTStore = true;  // streaming stores (outputs are written once)
 
 // ---------------------------------------------------------------------------
 // Block-FP8: one workgroup per 128 x 128 tile.  Thread t loads 8 rows
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
                                            f2 / div, f3 / div);   // IEEE fp32 divisions
             }
         }
-        if (cin && r < rows) *reinterpret_cast<uint2 *>(q + r * cols + col) = make_uint2(c[0], c[1]);
+        if (cin && r < rows) st8<kNTStore>(q + r * cols + col, make_uint2(c[0], c[1]));
     }
 }
 
@@ -102,24 +103,11 @@ __device__ __forceinline__ uint32_t bf16_of_product(float p, uint32_t code_sign)
     return p != p ? (0x7FC0u | (code_sign ? 0x8000u : 0u)) : bf16_rne(p);
 }
 
-__global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__restrict__ q,
-                                                           const float *__restrict__ scale,
-                                                           int64_t rows, int64_t cols,
-                                                           uint16_t *__restrict__ out, int64_t tc,
-                                                           int64_t nchunk)
+// One 8-element chunk of block-FP8 codes -> 8 bf16 (two words of 4 codes).
+__device__ __forceinline__ uint4 bfp8_dequant8(uint2 c, float S, bool slow)
 {
-    // Flat over 8-element chunks: chunk -> (row, col), cols % 8 == 0.
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nchunk) return;
-    const int64_t cpr = cols >> 3;
-    const int64_t r = i / cpr;
-    const int64_t col = (i - r * cpr) * 8;
-    const float S = scale[(r / kBlk) * tc + col / kBlk];
-    const uint2 c = *reinterpret_cast<const uint2 *>(q + r * cols + col);
-    const uint32_t tx = c.x & 0x7F7F7F7Fu, ty = c.y & 0x7F7F7F7Fu;
-    const bool nan_code = (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
     uint32_t o[4];
-    if (!wave_any(nan_code || !__builtin_isfinite(S))) {   // NaN products need the sign rule
+    if (!slow) {
         // E4M3 -> fp32 exactly (v_cvt_pk_f32_fp8), one fp32 product, RNE to bf16
         const uint32_t cw[2] = {c.x, c.y};
 #pragma unroll
@@ -140,7 +128,45 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
             o[j / 2] = bf16_of_product(p0, c0 & 0x80u) | (bf16_of_product(p1, c1 & 0x80u) << 16);
         }
     }
-    *reinterpret_cast<uint4 *>(out + r * cols + col) = make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Tiles: 512-column segment x 32 rows (4 waves x 8 rows); a 32-row block lies
+// inside one 128-row tile row, so each lane needs one scale.
+__global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__restrict__ q,
+                                                           const float *__restrict__ scale,
+                                                           int64_t rows, int64_t cols,
+                                                           uint16_t *__restrict__ out, int64_t tc,
+                                                           int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSegNv + lane * 8;
+    if (col >= cols) return;  // cols % 8 == 0; no barriers below
+    const int64_t r0 = rb * kRowsNv + wave;
+    const float S = scale[((rb * kRowsNv) / kBlk) * tc + col / kBlk];
+    constexpr int kR = kRowsNv / 4;
+    uint2 c[kR];
+    bool nan_code = false;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        c[i] = make_uint2(0, 0);
+        if (r < rows) c[i] = *reinterpret_cast<const uint2 *>(q + r * cols + col);
+        const uint32_t tx = c[i].x & 0x7F7F7F7Fu, ty = c[i].y & 0x7F7F7F7Fu;
+        nan_code |= (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
+    }
+    // NaN products (NaN code, NaN or infinite scale) take the exact sign rule
+    const bool slow = wave_any(nan_code || !__builtin_isfinite(S));
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        const uint4 o = slow ? bfp8_dequant8(c[i], S, true) : bfp8_dequant8(c[i], S, false);
+        if (r < rows) st16<kNTStore>(out + r * cols + col, o);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -154,10 +180,19 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restr
                                                          int64_t nvec, uint32_t *ws)
 {
     __shared__ uint32_t red[4];
+    constexpr int kU = 8;  // 16-byte loads in flight per thread
+    const uint4 *xv = reinterpret_cast<const uint4 *>(x);
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride)
-        m = max(m, amax8(reinterpret_cast<const uint4 *>(x)[i]));
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + (kU - 1) * stride < nvec; i += kU * stride) {
+        uint4 v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) m = max(m, amax8(v[u]));
+    }
+    for (; i < nvec; i += stride) m = max(m, amax8(xv[i]));
     m = wave_max(m);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
     __syncthreads();
@@ -187,11 +222,19 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
     const float d = 6.0f * g;
     if (tile == 0 && threadIdx.x == 0) *g_out = nonfinite ? __builtin_nanf("") : g;
 
-    for (int i = 0; i < kRowsNv / 4; ++i) {
+    constexpr int kR = kRowsNv / 4;  // rows per wave, all loads issued first
+    uint4 vv[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
         const int64_t r = rb * kRowsNv + wave + 4 * i;
-        uint4 v = make_uint4(0, 0, 0, 0);
+        vv[i] = make_uint4(0, 0, 0, 0);
+        if (cin && r < rows) vv[i] = *reinterpret_cast<const uint4 *>(x + r * cols + col);
+    }
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = rb * kRowsNv + wave + 4 * i;
         const bool ok = cin && r < rows;
-        if (ok) v = *reinterpret_cast<const uint4 *>(x + r * cols + col);
+        const uint4 v = vv[i];
         const uint32_t b8 = amax8(v);
         const uint32_t b = max(b8, dpp_swap1(b8));        // amax of the 16-block
         uint32_t s;
@@ -236,30 +279,17 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
             }
         }
         if (ok) {
-            *reinterpret_cast<uint32_t *>(q + r * (cols >> 1) + (col >> 1)) = packed;
+            st4<kNTStore>(q + r * (cols >> 1) + (col >> 1), packed);
             if ((lane & 1) == 0) s_out[r * (cols >> 4) + (col >> 4)] = (uint8_t)s;
         }
     }
 }
 
-__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__restrict__ q,
-                                                            const uint8_t *__restrict__ s_in,
-                                                            const float *__restrict__ g_in,
-                                                            int64_t rows, int64_t cols,
-                                                            uint16_t *__restrict__ out,
-                                                            int64_t nchunk)
+// 8 packed E2M1 nibbles (one word) -> 8 bf16, effective scale eff.
+__device__ __forceinline__ uint4 nvfp4_dequant8(uint32_t packed, float eff, bool slow)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= nchunk) return;
-    const int64_t cpr = cols >> 3;
-    const int64_t r = i / cpr;
-    const int64_t col = (i - r * cpr) * 8;
-    const float g = *g_in;
-    const uint32_t sb = s_in[r * (cols >> 4) + (col >> 4)];
-    const float eff = e4m3_to_f32(sb) * g;                 // one IEEE fp32 multiplication
-    const uint32_t packed = *reinterpret_cast<const uint32_t *>(q + r * (cols >> 1) + (col >> 1));
     uint32_t o[4];
-    if (!wave_any(!__builtin_isfinite(eff))) {   // NaN products (x * NaN, 0 * Inf) need the sign rule
+    if (!slow) {
         // E2M1 -> fp32 exactly (v_cvt_scalef32_pk_f32_fp4, scale 1), one product, RNE
         const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
         const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 1);
@@ -281,7 +311,47 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__res
             o[j] = bf16_of_product(q0, n0 & 8u) | (bf16_of_product(q1, n1 & 8u) << 16);
         }
     }
-    *reinterpret_cast<uint4 *>(out + r * cols + col) = make_uint4(o[0], o[1], o[2], o[3]);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__restrict__ q,
+                                                            const uint8_t *__restrict__ s_in,
+                                                            const float *__restrict__ g_in,
+                                                            int64_t rows, int64_t cols,
+                                                            uint16_t *__restrict__ out,
+                                                            int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSegNv + lane * 8;
+    if (col >= cols) return;  // cols % 16 == 0; no barriers below
+    const int64_t r0 = rb * kRowsNv + wave;
+    const float g = *g_in;
+    constexpr int kR = kRowsNv / 4;
+    uint32_t pk[kR];
+    float eff[kR];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        pk[i] = 0u;
+        eff[i] = 0.0f;
+        if (r < rows) {
+            pk[i] = *reinterpret_cast<const uint32_t *>(q + r * (cols >> 1) + (col >> 1));
+            eff[i] = e4m3_to_f32(s_in[r * (cols >> 4) + (col >> 4)]) * g;  // one IEEE fp32 multiplication
+        }
+        bad |= !__builtin_isfinite(eff[i]);  // NaN products (x * NaN, 0 * Inf) take the sign rule
+    }
+    const bool slow = wave_any(bad);
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        const uint4 o = slow ? nvfp4_dequant8(pk[i], eff[i], true) : nvfp4_dequant8(pk[i], eff[i], false);
+        if (r < rows) st16<kNTStore>(out + r * cols + col, o);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -302,13 +372,13 @@ hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint
 hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
                                uint16_t *out, hipStream_t stream)
 {
-    const int64_t nchunk = rows * (cols / 8);
-    if (nchunk <= 0) return hipSuccess;
-    const int64_t blocks = (nchunk + 255) / 256;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
+    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const int64_t tc = (cols + kBlk - 1) / kBlk;
-    hipLaunchKernelGGL(bfp8_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, scale,
-                       rows, cols, out, tc, nchunk);
+    hipLaunchKernelGGL(bfp8_dequant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scale,
+                       rows, cols, out, tc, nseg);
     return hipGetLastError();
 }
 
@@ -336,12 +406,12 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
 hipError_t launch_nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *g, int64_t rows,
                                 int64_t cols, uint16_t *out, hipStream_t stream)
 {
-    const int64_t nchunk = rows * (cols / 8);
-    if (nchunk <= 0) return hipSuccess;
-    const int64_t blocks = (nchunk + 255) / 256;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q, s, g,
-                       rows, cols, out, nchunk);
+    const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
+    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, s, g,
+                       rows, cols, out, nseg);
     return hipGetLastError();
 }
 

@@ -365,6 +365,53 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_f32(uint32_t old, float a, float b
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, kByte);
 }
 
+// ---------------------------------------------------------------------------
+// Global memory access with an optional non-temporal (streaming) hint: every
+// byte here is touched once, so keeping it out of the caches' working set
+// can only help.  kNT selects the hinted form.
+// ---------------------------------------------------------------------------
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+template <bool kNT>
+__device__ __forceinline__ uint4 ld16(const void *p)
+{
+    if (kNT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+template <bool kNT>
+__device__ __forceinline__ void st16(void *p, uint4 v)
+{
+    if (kNT) {
+        const u32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+    } else {
+        *reinterpret_cast<uint4 *>(p) = v;
+    }
+}
+
+template <bool kNT>
+__device__ __forceinline__ void st8(void *p, uint2 v)
+{
+    if (kNT) {
+        const u32x2_t w = {v.x, v.y};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t *>(p));
+    } else {
+        *reinterpret_cast<uint2 *>(p) = v;
+    }
+}
+
+template <bool kNT>
+__device__ __forceinline__ void st4(void *p, uint32_t v)
+{
+    if (kNT) __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(p));
+    else *reinterpret_cast<uint32_t *>(p) = v;
+}
+
 // Wave-uniform OR of a lane predicate.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
