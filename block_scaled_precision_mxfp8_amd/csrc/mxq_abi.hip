@@ -134,8 +134,11 @@ mxq_status mxq_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, int axi
 
 size_t mxq_grouped_workspace_size(int32_t n)
 {
-    return n <= 0 ? 0 : (size_t)n * sizeof(GroupEntry);
+    // [GroupEntry x n][int32 first tile x n], rounded up to 16 bytes
+    return n <= 0 ? 0 : ((size_t)n * (sizeof(GroupEntry) + sizeof(int32_t)) + 15) / 16 * 16;
 }
+
+size_t nvfp4_workspace_size(void) { return (size_t)mxq::kNvAmaxBlocks * sizeof(uint32_t); }
 
 mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n, void *workspace,
                                         size_t workspace_bytes, void *stream)
@@ -146,7 +149,9 @@ mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n, 
     if (!aligned(workspace, 16)) return MXQ_EALIGN;
     if (workspace_bytes < mxq_grouped_workspace_size(n)) return MXQ_ESIZE;
     std::vector<GroupEntry> table;
+    std::vector<int32_t> starts;
     table.reserve((size_t)n);
+    starts.reserve((size_t)n);
     int64_t tiles = 0;
     for (int32_t i = 0; i < n; ++i) {
         const mxq_group_desc &d = descs[i];
@@ -165,15 +170,24 @@ mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n, 
         e.lds = d.lds;
         e.tile_begin = tiles;
         const int64_t t = mxq::mx_row_tiles(d.rows, d.cols, &e.nseg);
-        if (__builtin_add_overflow(tiles, t, &tiles)) return MXQ_ESIZE;
+        if (__builtin_add_overflow(tiles, t, &tiles) || tiles > 0x7FFFFFFF) return MXQ_ESIZE;
         table.push_back(e);
+        starts.push_back((int32_t)e.tile_begin);
     }
     if (table.empty()) return MXQ_OK;
-    // Pageable source: the copy has consumed `table` by the time it returns.
-    hipError_t err = hipMemcpyAsync(workspace, table.data(), table.size() * sizeof(GroupEntry),
-                                    hipMemcpyHostToDevice, as_stream(stream));
+    // One staging buffer: the table, then the first-tile array right after the
+    // n entries the workspace was sized for.  Pageable source: the copy has
+    // consumed it by the time hipMemcpyAsync returns.
+    const size_t tbytes = (size_t)n * sizeof(GroupEntry);
+    std::vector<unsigned char> stage(tbytes + starts.size() * sizeof(int32_t));
+    memcpy(stage.data(), table.data(), table.size() * sizeof(GroupEntry));
+    memcpy(stage.data() + tbytes, starts.data(), starts.size() * sizeof(int32_t));
+    hipError_t err = hipMemcpyAsync(workspace, stage.data(), stage.size(), hipMemcpyHostToDevice,
+                                    as_stream(stream));
     if (err != hipSuccess) return MXQ_EHIP;
-    return from_hip(mxq::launch_mx_grouped(static_cast<const GroupEntry *>(workspace),
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    return from_hip(mxq::launch_mx_grouped(reinterpret_cast<const GroupEntry *>(ws),
+                                           reinterpret_cast<const int32_t *>(ws + tbytes),
                                            (int32_t)table.size(), tiles, as_stream(stream)));
 }
 
@@ -209,7 +223,7 @@ mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t
     if (cols % 16 != 0) return MXQ_ESHAPE;
     if (rows == 0 || cols == 0) return MXQ_OK;
     if (!x || !q_packed || !s_e4m3 || !global_scale || !workspace) return MXQ_EINVAL;
-    if (workspace_bytes < 4) return MXQ_ESIZE;
+    if (workspace_bytes < nvfp4_workspace_size()) return MXQ_ESIZE;
     if (!aligned(x, 16) || !aligned(q_packed, 4) || !aligned(global_scale, 4) ||
         !aligned(workspace, 4))
         return MXQ_EALIGN;

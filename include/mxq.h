@@ -180,10 +180,14 @@ mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t row
  *   q_packed   [rows, cols/2] bytes, contiguous, 4-byte aligned
  *   s_e4m3     [rows, cols/16] E4M3 bytes, contiguous
  *   global_scale  one float (device), written with g
- *   workspace  >= 4 bytes of device memory, 4-byte aligned, caller-owned,
- *              used for the tensor-wide amax between two launches
+ *   workspace  >= nvfp4_workspace_size() bytes of device memory, 4-byte
+ *              aligned, caller-owned: per-workgroup partial maxima passed
+ *              between the two launches (no initial contents needed; calls
+ *              that overlap on one workspace race)
  * Shape: cols % 16 == 0.
  */
+size_t nvfp4_workspace_size(void);
+
 mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
                           uint8_t *s_e4m3, float *global_scale, void *workspace,
                           size_t workspace_bytes, void *stream);

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     for want in ["mxq_quantize_rowwise", "mxq_quantize_colwise", "mxq_dequantize", "mxq_fake_quant",
                  "mxq_quantize_rowwise_grouped", "blockfp8_quantize", "blockfp8_dequantize",
                  "nvfp4_quantize", "nvfp4_dequantize", "mxq_status_string", "mxq_abi_version",
-                 "mxq_grouped_workspace_size"]:
+                 "mxq_grouped_workspace_size", "nvfp4_workspace_size"]:
         assert want in names
     assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
 
@@ -108,7 +108,7 @@ def test_grouped_errors(lib):
     g = lib.mxq_quantize_rowwise_grouped
     assert lib.mxq_grouped_workspace_size(0) == 0
     ws = lib.mxq_grouped_workspace_size(3)
-    assert ws >= 3 * 64
+    assert ws >= 3 * 84 and ws % 16 == 0
     descs = (mxq.GroupDesc * 3)()
     for i in range(3):
         descs[i] = mxq.GroupDesc(0x10000, 0x20000, 0x30000, 8, 64, 64, 64, 2)
@@ -137,11 +137,13 @@ def test_blockfp8_nvfp4_errors(lib):
     assert bd(P16, P16, 4, 64, 128, P8, NULL) == mxq.MXQ_EALIGN
     assert bd(P16, NULL, 4, 64, 128, P16, NULL) == mxq.MXQ_EINVAL
     n = lib.nvfp4_quantize
-    assert n(P16, 4, 24, P16, P16, P16, P16, 4, NULL) == mxq.MXQ_ESHAPE          # cols % 16
-    assert n(P16, 4, 32, P16, P16, P16, NULL, 4, NULL) == mxq.MXQ_EINVAL         # no workspace
-    assert n(P16, 4, 32, P16, P16, P16, P16, 2, NULL) == mxq.MXQ_ESIZE
-    assert n(P8, 4, 32, P16, P16, P16, P16, 4, NULL) == mxq.MXQ_EALIGN
-    assert n(P16, 4, 32, P2, P16, P16, P16, 4, NULL) == mxq.MXQ_EALIGN
+    W = lib.nvfp4_workspace_size()
+    assert W >= 4
+    assert n(P16, 4, 24, P16, P16, P16, P16, W, NULL) == mxq.MXQ_ESHAPE          # cols % 16
+    assert n(P16, 4, 32, P16, P16, P16, NULL, W, NULL) == mxq.MXQ_EINVAL         # no workspace
+    assert n(P16, 4, 32, P16, P16, P16, P16, W - 1, NULL) == mxq.MXQ_ESIZE
+    assert n(P8, 4, 32, P16, P16, P16, P16, W, NULL) == mxq.MXQ_EALIGN
+    assert n(P16, 4, 32, P2, P16, P16, P16, W, NULL) == mxq.MXQ_EALIGN
     nd = lib.nvfp4_dequantize
     assert nd(P16, P16, NULL, 4, 32, P16, NULL) == mxq.MXQ_EINVAL
     assert nd(P16, P16, P16, 4, 32, P8, NULL) == mxq.MXQ_EALIGN

@@ -399,3 +399,30 @@ def test_fp_dequant_arbitrary_codes(gpu, orc):
                                   torch.from_numpy(g).cuda())
         torch.cuda.synchronize()
         assert_same(f"nvfp4 dq g={gval}", bits16(dq), orc.nvfp4_dequantize(qp, s, g))
+
+
+def test_workspaces_need_no_initial_contents(gpu, orc):
+    """A workspace reused across calls (second call smaller) or filled with
+    garbage gives the same bytes as the oracle."""
+    ws = gpu.nvfp4_workspace("cuda")
+    ws.fill_(0xFF)
+    for shape, seed in (((256, 1024), 31), ((40, 64), 32)):
+        xb = workloads.random_bf16(shape, seed)
+        announce(f"nvfp4 workspace reuse {shape}")
+        q, s, g = gpu.nvfp4_quantize(to_dev_bf16(xb), workspace=ws)
+        torch.cuda.synchronize()
+        oq, os_, og = orc.nvfp4_quantize(xb)
+        assert_same(f"ws {shape} q", u8(q), oq)
+        assert_same(f"ws {shape} s", u8(s), os_)
+        assert_same(f"ws {shape} g", f32bits(g), f32bits(og))
+    gws = gpu.grouped_workspace(3, "cuda")
+    gws.fill_(0xA5)
+    for shapes, seed in (([(64, 512), (33, 96), (100, 2048)], 41), ([(7, 32)], 42)):
+        xs_b = [workloads.random_bf16(sh, seed + i) for i, sh in enumerate(shapes)]
+        announce(f"grouped workspace reuse {shapes}")
+        outs = gpu.quantize_rowwise_grouped([to_dev_bf16(b) for b in xs_b], workspace=gws)
+        torch.cuda.synchronize()
+        for b, (q, s) in zip(xs_b, outs):
+            oq, os_ = orc.mxfp8_quantize_rowwise(b)
+            assert_same("grouped reuse q", u8(q), oq)
+            assert_same("grouped reuse s", u8(s), os_)
