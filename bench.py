@@ -1,12 +1,17 @@
 #!/usr/bin/env python3
 """Throughput of the MXFP8 quantizer on one MI355X.
 
-One step = one pass of the hot path over the [16384, 7168] bf16 activation
-(0.5 * Student-t(3), seeded): MXFP8 column-wise (groups of 32 tokens),
+One step = one pass of the hot path over one [16384, 7168] bf16 activation
+batch (0.5 * Student-t(3), seeded): MXFP8 column-wise (groups of 32 tokens),
 row-wise (groups of 32 along hidden) and the fused row-wise fake-quant, all
 from a single read of the input.  ``value`` is algorithmic bytes (bf16 in +
 codes, scales and fake-quant out) per second over the timed steps, inputs
 resident in HBM.  Prints one JSON line.
+
+Steps cycle through BATCHES resident batches, each with its own outputs
+(distinct HBM addresses, 2.8 GB in all), so no step finds its input in the
+256 MB Infinity Cache that the previous step just streamed through: the
+timed rate is an HBM rate.  Every other workload is timed the same way.
 
 Besides the timed steps it reports, in the same line:
   roofline      the one-pass kernel's achieved GB/s (HIP events on the stream
@@ -25,7 +30,6 @@ import ctypes
 import hashlib
 import json
 import os
-import statistics
 import sys
 import time
 
@@ -33,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+BATCHES = 4            # resident batches the main step loop cycles through
+ROTATE_BYTES = 1e9     # other workloads: enough copies to touch this much between reuses
 METRIC = "MXFP8 quantize GB/s (bf16 in + fp8/scale out) and % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_mxfp8_amd", "csrc", f)
@@ -75,7 +81,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-breakdown", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
+    ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="rows of the activation the CPU oracle baseline processes")
     args = ap.parse_args()
 
@@ -114,22 +120,28 @@ def main():
     rows, cols = workloads.SHAPES["act_16384"]
     log(f"generating act_16384 [{rows}, {cols}]")
     xb = workloads.act_16384()
-    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    x0 = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
     e = rows * cols
-    qc = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    sc = torch.empty(((rows + 31) // 32, cols), dtype=torch.uint8, device=dev)
-    qr = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    sr = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
-    fq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-    step_bytes = 2 * e + e + e // 32 + e + sc.numel() + 2 * e
 
-    def step():
-        check(lib.mxq_quantize_colwise(P(x), rows, cols, P(qc), P(sc), P(qr), P(sr), P(fq), sp),
-              "mxq_quantize_colwise")
+    def batch(src):
+        return {"x": src.clone(),
+                "qc": torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                "sc": torch.empty(((rows + 31) // 32, cols), dtype=torch.uint8, device=dev),
+                "qr": torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                "sr": torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
+                "fq": torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)}
+
+    batches = [batch(x0) for _ in range(BATCHES)]
+    del x0
+    step_bytes = 2 * e + e + e // 32 + e + batches[0]["sc"].numel() + 2 * e
+
+    def launch_fused(d):
+        check(lib.mxq_quantize_colwise(P(d["x"]), rows, cols, P(d["qc"]), P(d["sc"]), P(d["qr"]),
+                                       P(d["sr"]), P(d["fq"]), sp), "mxq_quantize_colwise")
 
     log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, BATCHES)):
+        launch_fused(batches[i % BATCHES])
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
@@ -137,8 +149,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        launch_fused(batches[i % BATCHES])
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -156,7 +168,7 @@ def main():
     torch.cuda.synchronize()
     evs[0].record(stream)
     for i in range(nl):
-        step()
+        launch_fused(batches[i % BATCHES])
         evs[i + 1].record(stream)
     evs[-1].synchronize()
     durs = [evs[i].elapsed_time(evs[i + 1]) for i in range(nl)]
@@ -169,22 +181,22 @@ def main():
                 "per_launch_us_min_max": [round(min(durs) * 1e3, 2), round(max(durs) * 1e3, 2)]}
     log(f"main: {value:.1f} GB/s per step, kernel {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
 
-    # plain device copy of the same byte count: the practical ceiling
+    # plain device copy of the same byte count, cycled the same way: the
+    # practical ceiling of a read/write stream
     half = step_bytes // 2
-    src = torch.empty(half, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    cdur = []
-    for _ in range(10):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        dst.copy_(src)
-        b.record(stream)
-        b.synchronize()
-        cdur.append(a.elapsed_time(b))
-    copy_gbs = 2 * half / (statistics.median(cdur) * 1e-3) / 1e9
-    del src, dst
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev),
+              torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(BATCHES)]
+    for i in range(BATCHES):
+        pairs[i][1].copy_(pairs[i][0])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(20):
+        pairs[i % BATCHES][1].copy_(pairs[i % BATCHES][0])
+    b.record(stream)
+    b.synchronize()
+    copy_gbs = 2 * half / (a.elapsed_time(b) / 20 * 1e-3) / 1e9
+    del pairs
 
     # ------------------------------------------------------------------
     # CPU oracle on a bounded sample (first cpu_rows rows, same arithmetic)
@@ -203,82 +215,83 @@ def main():
         dt = time.perf_counter() - t
         sbytes = 2 * se + se + se // 32 + se + ((args.cpu_rows + 31) // 32) * cols + 2 * se
         cpu = {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {args.cpu_rows} of {rows} rows of the same input: row-wise + "
-                         f"column-wise quantize and row-wise dequantize, {dt:.1f} s single-threaded"}
+               "sample": f"{args.cpu_rows} of {rows} rows of the same batch: row-wise + "
+                         f"column-wise quantize and row-wise dequantize (the step's outputs), "
+                         f"{dt:.1f} s single-threaded"}
 
     # ------------------------------------------------------------------
     # breakdown: every other workload, timed on its own
     # ------------------------------------------------------------------
     breakdown = {}
     if not args.no_breakdown:
-        # Inputs under 256 MB would sit in the Infinity Cache between repeats:
-        # before each timed launch, read 1 GiB (a read leaves no dirty lines
-        # whose write-back would land in the timed kernel).
-        flush = torch.ones(256 * 1024 * 1024, dtype=torch.int32, device=dev)
-
-        def timed(fn, nbytes, iters=20, flush_cache=True):
-            for _ in range(3):
+        def rotated(launches, nbytes, iters=20):
+            """Back-to-back launches cycling through copies with their own
+            buffers; per-launch time = total / iters."""
+            for fn in launches:
                 fn()
-            ts = []
-            for _ in range(iters):
-                if flush_cache:
-                    flush.max()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
-                b.synchronize()
-                ts.append(a.elapsed_time(b))
-            ms = statistics.median(ts)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(iters):
+                launches[i % len(launches)]()
+            b.record(stream)
+            b.synchronize()
+            ms = a.elapsed_time(b) / iters
             gbs = nbytes / (ms * 1e-3) / 1e9
             return {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(nbytes)}
+                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(nbytes),
+                    "copies": len(launches)}
 
-        # the main tensor, one output family at a time
-        breakdown["act_16384 row-wise only"] = timed(
-            lambda: check(lib.mxq_quantize_rowwise(P(x), rows, cols, cols, P(qr), cols, P(sr),
-                                                   cols // 32, None, 0, sp), "rowwise"),
-            2 * e + e + e // 32, flush_cache=False)
-        breakdown["act_16384 column-wise only"] = timed(
-            lambda: check(lib.mxq_quantize_colwise(P(x), rows, cols, P(qc), P(sc), None, None,
-                                                   None, sp), "colwise"),
-            2 * e + e + sc.numel(), flush_cache=False)
-        breakdown["act_16384 fake-quant only"] = timed(
-            lambda: check(lib.mxq_fake_quant(P(x), rows, cols, 1, P(fq), sp), "fake_quant"),
-            4 * e, flush_cache=False)
-        del qc, sc, fq
+        def ncopies(nbytes):
+            return int(min(8, max(2, -(-ROTATE_BYTES // nbytes))))
+
+        # the main tensor, one output family at a time (same batches)
+        rb = 2 * e + e + e // 32
+        breakdown["act_16384 row-wise only"] = rotated(
+            [lambda d=d: check(lib.mxq_quantize_rowwise(P(d["x"]), rows, cols, cols, P(d["qr"]),
+                                                        cols, P(d["sr"]), cols // 32, None, 0, sp),
+                               "rowwise") for d in batches], rb)
+        breakdown["act_16384 column-wise only"] = rotated(
+            [lambda d=d: check(lib.mxq_quantize_colwise(P(d["x"]), rows, cols, P(d["qc"]),
+                                                        P(d["sc"]), None, None, None, sp),
+                               "colwise") for d in batches], 2 * e + e + batches[0]["sc"].numel())
+        breakdown["act_16384 fake-quant only"] = rotated(
+            [lambda d=d: check(lib.mxq_fake_quant(P(d["x"]), rows, cols, 1, P(d["fq"]), sp),
+                               "fake_quant") for d in batches], 4 * e)
+        del batches
+        torch.cuda.empty_cache()
 
         # weight [4097, 7168] row-wise (pad-then-crop case)
         wb = workloads.weight_4097()
-        w = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(dev)
+        w0 = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(dev)
         wr, wc = wb.shape
-        wq = torch.empty((wr, wc), dtype=torch.uint8, device=dev)
-        ws = torch.empty((wr, wc // 32), dtype=torch.uint8, device=dev)
-        breakdown["weight_4097 row-wise"] = timed(
-            lambda: check(lib.mxq_quantize_rowwise(P(w), wr, wc, wc, P(wq), wc, P(ws), wc // 32,
-                                                   None, 0, sp), "rowwise"),
-            3 * wr * wc + wr * wc // 32)
-        del w, wq, ws
+        wbytes = 3 * wr * wc + wr * wc // 32
+        wsets = [(w0.clone(), torch.empty((wr, wc), dtype=torch.uint8, device=dev),
+                  torch.empty((wr, wc // 32), dtype=torch.uint8, device=dev))
+                 for _ in range(ncopies(wbytes))]
+        breakdown["weight_4097 row-wise"] = rotated(
+            [lambda t=t: check(lib.mxq_quantize_rowwise(P(t[0]), wr, wc, wc, P(t[1]), wc, P(t[2]),
+                                                        wc // 32, None, 0, sp), "rowwise")
+             for t in wsets], wbytes)
+        del w0, wsets
 
-        # mx_small row-wise + dequantize
+        # mx_small row-wise + dequantize: a latency measurement (the data is
+        # cache-resident at this size whatever is done)
         mb = workloads.mx_small()
         m = torch.from_numpy(mb.view(np.int16)).view(torch.bfloat16).to(dev)
         mq = torch.empty(mb.shape, dtype=torch.uint8, device=dev)
         ms_ = torch.empty((mb.shape[0], mb.shape[1] // 32), dtype=torch.uint8, device=dev)
         md = torch.empty(mb.shape, dtype=torch.bfloat16, device=dev)
         me = mb.size
-        breakdown["mx_small row-wise"] = timed(
-            lambda: check(lib.mxq_quantize_rowwise(P(m), mb.shape[0], mb.shape[1], mb.shape[1],
-                                                   P(mq), mb.shape[1], P(ms_), mb.shape[1] // 32,
-                                                   None, 0, sp), "rowwise"),
-            3 * me + me // 32)
-        breakdown["mx_small dequantize"] = timed(
-            lambda: check(lib.mxq_dequantize(P(mq), P(ms_), mb.shape[0], mb.shape[1], 1, P(md), sp),
-                          "dequantize"), 3 * me + me // 32)
+        breakdown["mx_small row-wise"] = rotated(
+            [lambda: check(lib.mxq_quantize_rowwise(P(m), mb.shape[0], mb.shape[1], mb.shape[1],
+                                                    P(mq), mb.shape[1], P(ms_), mb.shape[1] // 32,
+                                                    None, 0, sp), "rowwise")], 3 * me + me // 32)
+        breakdown["mx_small dequantize"] = rotated(
+            [lambda: check(lib.mxq_dequantize(P(mq), P(ms_), mb.shape[0], mb.shape[1], 1, P(md),
+                                              sp), "dequantize")], 3 * me + me // 32)
 
-        # grouped MoE experts: 384 tensors, one launch
-        del x, qr, sr
-        torch.cuda.empty_cache()
+        # grouped MoE experts: 384 tensors (11.3 GB in), one launch
         shapes = workloads.moe_shapes()
         mult = workloads.moe_multipliers()
         log("generating moe_experts (384 tensors)")
@@ -292,38 +305,48 @@ def main():
         wsz = lib.mxq_grouped_workspace_size(len(xs))
         gws = torch.empty(wsz, dtype=torch.uint8, device=dev)
         ge = sum(r * c for (_, r, c) in shapes)
-        breakdown["moe_experts grouped row-wise"] = timed(
-            lambda: check(lib.mxq_quantize_rowwise_grouped(descs, len(xs), P(gws), wsz, sp),
-                          "grouped"), 3 * ge + ge // 32, iters=10, flush_cache=False)
+        breakdown["moe_experts grouped row-wise"] = rotated(
+            [lambda: check(lib.mxq_quantize_rowwise_grouped(descs, len(xs), P(gws), wsz, sp),
+                           "grouped")], 3 * ge + ge // 32, iters=10)
         del xs, outs, gws
         torch.cuda.empty_cache()
 
         # square [8192, 8192]: block-FP8 and NVFP4, quantize and dequantize
         yb = workloads.square_8192()
-        y = torch.from_numpy(yb.view(np.int16)).view(torch.bfloat16).to(dev)
+        y0 = torch.from_numpy(yb.view(np.int16)).view(torch.bfloat16).to(dev)
         n_ = yb.shape[0]
         ye = yb.size
-        bq = torch.empty((n_, n_), dtype=torch.uint8, device=dev)
-        bS = torch.empty((n_ // 128, n_ // 128), dtype=torch.float32, device=dev)
-        bd = torch.empty((n_, n_), dtype=torch.bfloat16, device=dev)
-        breakdown["square_8192 block-FP8 quantize"] = timed(
-            lambda: check(lib.blockfp8_quantize(P(y), n_, n_, 128, P(bq), P(bS), sp), "bfp8"),
-            3 * ye + 4 * bS.numel())
-        breakdown["square_8192 block-FP8 dequantize"] = timed(
-            lambda: check(lib.blockfp8_dequantize(P(bq), P(bS), n_, n_, 128, P(bd), sp), "bfp8 dq"),
-            3 * ye + 4 * bS.numel())
-        nq = torch.empty((n_, n_ // 2), dtype=torch.uint8, device=dev)
-        ns = torch.empty((n_, n_ // 16), dtype=torch.uint8, device=dev)
-        ng = torch.empty((1,), dtype=torch.float32, device=dev)
         nwsz = lib.nvfp4_workspace_size()
-        nws = torch.empty((nwsz,), dtype=torch.uint8, device=dev)
-        breakdown["square_8192 NVFP4 quantize (unique bytes)"] = timed(
-            lambda: check(lib.nvfp4_quantize(P(y), n_, n_, P(nq), P(ns), P(ng), P(nws), nwsz, sp),
-                          "nvfp4"), 2 * ye + ye // 2 + ye // 16 + 4)
-        breakdown["square_8192 NVFP4 dequantize"] = timed(
-            lambda: check(lib.nvfp4_dequantize(P(nq), P(ns), P(ng), n_, n_, P(bd), sp), "nvfp4 dq"),
-            ye // 2 + ye // 16 + 4 + 2 * ye)
-        del flush
+        bbytes = 3 * ye + 4 * (n_ // 128) ** 2
+        nbytes = 2 * ye + ye // 2 + ye // 16 + 4
+        ysets = []
+        for _ in range(ncopies(bbytes)):
+            ysets.append({
+                "y": y0.clone(),
+                "bq": torch.empty((n_, n_), dtype=torch.uint8, device=dev),
+                "bS": torch.empty((n_ // 128, n_ // 128), dtype=torch.float32, device=dev),
+                "bd": torch.empty((n_, n_), dtype=torch.bfloat16, device=dev),
+                "nq": torch.empty((n_, n_ // 2), dtype=torch.uint8, device=dev),
+                "ns": torch.empty((n_, n_ // 16), dtype=torch.uint8, device=dev),
+                "ng": torch.empty((1,), dtype=torch.float32, device=dev),
+                "nws": torch.empty((nwsz,), dtype=torch.uint8, device=dev)})
+        del y0
+        breakdown["square_8192 block-FP8 quantize"] = rotated(
+            [lambda d=d: check(lib.blockfp8_quantize(P(d["y"]), n_, n_, 128, P(d["bq"]), P(d["bS"]),
+                                                     sp), "bfp8") for d in ysets], bbytes)
+        breakdown["square_8192 block-FP8 dequantize"] = rotated(
+            [lambda d=d: check(lib.blockfp8_dequantize(P(d["bq"]), P(d["bS"]), n_, n_, 128,
+                                                       P(d["bd"]), sp), "bfp8 dq") for d in ysets],
+            bbytes)
+        breakdown["square_8192 NVFP4 quantize (unique bytes)"] = rotated(
+            [lambda d=d: check(lib.nvfp4_quantize(P(d["y"]), n_, n_, P(d["nq"]), P(d["ns"]),
+                                                  P(d["ng"]), P(d["nws"]), nwsz, sp), "nvfp4")
+             for d in ysets], nbytes)
+        breakdown["square_8192 NVFP4 dequantize"] = rotated(
+            [lambda d=d: check(lib.nvfp4_dequantize(P(d["nq"]), P(d["ns"]), P(d["ng"]), n_, n_,
+                                                    P(d["bd"]), sp), "nvfp4 dq") for d in ysets],
+            nbytes)
+        del ysets
 
     out = {
         "metric": METRIC,
@@ -341,6 +364,7 @@ def main():
         "config": {"workload": "act_16384: bf16 [16384, 7168], 0.5*Student-t(3), seed 3; MXFP8 "
                                "column-wise + row-wise + fused row-wise fake-quant in one pass",
                    "rows": rows, "cols": cols, "bytes_per_step": step_bytes,
+                   "resident_batches": BATCHES,
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "wall_s_timed": round(wall, 4),

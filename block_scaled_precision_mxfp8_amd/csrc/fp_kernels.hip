@@ -20,7 +20,16 @@ namespace mxq {
 constexpr int kBlk = 128;   // block-FP8 tile edge
 constexpr int kSegNv = 512; // NVFP4 columns per wave segment (64 lanes x 8)
 constexpr int kRowsNv = 32; // NVFP4 rows per workgroup tile
-constexpr bool kNTStore = true;  // streaming stores (outputs are written once)
+// Streaming (non-temporal) hints, chosen by measurement on MI355X with
+// inputs read cold from HBM.  Outputs are written once.  Hinted 16-byte loads
+// of x help block-FP8 (+3%); the dequantizers' 4- and 8-byte code loads do
+// better unhinted (NVFP4: 4.3 -> 5.0 TB/s).  The NVFP4 amax pass loads
+// unhinted so that x can stay in the Infinity Cache for the encoding pass.
+constexpr bool kNTStore = true;
+constexpr bool kNTLoad = true;
+constexpr bool kNTLoadDq = false;
+constexpr bool kNTLoadNvAmax = false;
+constexpr bool kNTLoadNvQuant = true;
 
 // ---------------------------------------------------------------------------
 // Block-FP8: one workgroup per 128 x 128 tile.  Thread t loads 8 rows
@@ -44,7 +53,7 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
     for (int k = 0; k < 8; ++k) {
         const int64_t r = rbase + 16 * k;
         v[k] = make_uint4(0, 0, 0, 0);
-        if (cin && r < rows) v[k] = *reinterpret_cast<const uint4 *>(x + r * cols + col);
+        if (cin && r < rows) v[k] = ld16<kNTLoad>(x + r * cols + col);
         m = max(m, amax8(v[k]));
     }
     m = wave_max(m);
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
         c[i] = make_uint2(0, 0);
-        if (r < rows) c[i] = *reinterpret_cast<const uint2 *>(q + r * cols + col);
+        if (r < rows) c[i] = ld8<kNTLoadDq>(q + r * cols + col);
         const uint32_t tx = c[i].x & 0x7F7F7F7Fu, ty = c[i].y & 0x7F7F7F7Fu;
         nan_code |= (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
     }
@@ -172,11 +181,10 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
 // ---------------------------------------------------------------------------
 // NVFP4.  Pass 1: each workgroup writes the max magnitude (bf16 bits) of its
 // share of x to a partials array; pass 2 reduces the partials (an unsigned
-// max: order-independent, deterministic) and quantizes.  In pass 2 each lane
-// owns one whole 16-element block: 32 bytes of x, 8 bytes of packed codes
-// and its scale byte.
+// max: order-independent, deterministic) and quantizes.  In pass 2 a lane
+// pair owns one 16-element block: 16 bytes of x, 4 bytes of packed codes and
+// (both lanes) its scale byte each.
 // ---------------------------------------------------------------------------
-constexpr int kSegNv16 = 1024;   // columns per wave segment (64 lanes x 16)
 
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
                                                          int64_t nvec, uint32_t *__restrict__ partial)
@@ -190,42 +198,37 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restr
     for (; i + (kU - 1) * stride < nvec; i += kU * stride) {
         uint4 v[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) v[u] = xv[i + u * stride];
+        for (int u = 0; u < kU; ++u) v[u] = ld16<kNTLoadNvAmax>(xv + i + u * stride);
 #pragma unroll
         for (int u = 0; u < kU; ++u) m = max(m, amax8(v[u]));
     }
-    for (; i < nvec; i += stride) m = max(m, amax8(xv[i]));
+    for (; i < nvec; i += stride) m = max(m, amax8(ld16<kNTLoadNvAmax>(xv + i)));
     m = wave_max(m);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
     __syncthreads();
     if (threadIdx.x == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
-// The 16 E2M1 codes of one block (two words of x pairs) under effective scale
-// eff, 8 bytes packed (element 2j -> low nibble of byte j).
-__device__ __forceinline__ uint2 nvfp4_codes16(const uint4 a, const uint4 b, float eff, float y,
-                                               bool fast, bool nonfinite)
+// 8 E2M1 codes (half a block, four words of x pairs) under effective scale
+// eff, packed into one word (element 2j -> low nibble of byte j).
+__device__ __forceinline__ uint32_t nvfp4_codes8(const uint4 a, float eff, float y, bool fast,
+                                                 bool nonfinite)
 {
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t out[2] = {0u, 0u};
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+    uint32_t out = 0u;
     if (fast) {
         // reciprocal + FMA correction (exact here), E2M1 by the hardware
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint32_t p = 0u;
-            p = cvt_fp4x2_f32<0>(p, div_markstein(bf16lo_to_f32(w[4 * h + 0]), eff, y),
-                                 div_markstein(bf16hi_to_f32(w[4 * h + 0]), eff, y));
-            p = cvt_fp4x2_f32<1>(p, div_markstein(bf16lo_to_f32(w[4 * h + 1]), eff, y),
-                                 div_markstein(bf16hi_to_f32(w[4 * h + 1]), eff, y));
-            p = cvt_fp4x2_f32<2>(p, div_markstein(bf16lo_to_f32(w[4 * h + 2]), eff, y),
-                                 div_markstein(bf16hi_to_f32(w[4 * h + 2]), eff, y));
-            p = cvt_fp4x2_f32<3>(p, div_markstein(bf16lo_to_f32(w[4 * h + 3]), eff, y),
-                                 div_markstein(bf16hi_to_f32(w[4 * h + 3]), eff, y));
-            out[h] = p;
-        }
+        out = cvt_fp4x2_f32<0>(out, div_markstein(bf16lo_to_f32(w[0]), eff, y),
+                               div_markstein(bf16hi_to_f32(w[0]), eff, y));
+        out = cvt_fp4x2_f32<1>(out, div_markstein(bf16lo_to_f32(w[1]), eff, y),
+                               div_markstein(bf16hi_to_f32(w[1]), eff, y));
+        out = cvt_fp4x2_f32<2>(out, div_markstein(bf16lo_to_f32(w[2]), eff, y),
+                               div_markstein(bf16hi_to_f32(w[2]), eff, y));
+        out = cvt_fp4x2_f32<3>(out, div_markstein(bf16lo_to_f32(w[3]), eff, y),
+                               div_markstein(bf16hi_to_f32(w[3]), eff, y));
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const float f0 = bf16lo_to_f32(w[j]), f1 = bf16hi_to_f32(w[j]);
             uint32_t n0, n1;
             if (nonfinite) {
@@ -238,12 +241,15 @@ __device__ __forceinline__ uint2 nvfp4_codes16(const uint4 a, const uint4 b, flo
             }
             n0 |= (w[j] >> 12) & 0x8u;          // sign of the low bf16
             n1 |= (w[j] >> 28) & 0x8u;          // sign of the high bf16
-            out[j >> 2] |= (n0 | (n1 << 4)) << (8 * (j & 3));
+            out |= (n0 | (n1 << 4)) << (8 * j);
         }
     }
-    return make_uint2(out[0], out[1]);
+    return out;
 }
 
+// Tiles: 512-column segment x 32 rows (4 waves x 8 rows).  Lane pair
+// (2k, 2k+1) holds one 16-element block, 8 elements each, so every load and
+// store instruction of a wave is contiguous; the block amax is one DPP swap.
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
                                                           int64_t rows, int64_t cols,
                                                           uint8_t *__restrict__ q,
@@ -258,20 +264,17 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
     const int64_t rb = tile / nseg;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-    const int64_t col = seg * kSegNv16 + lane * 16;
-    const bool cin = col < cols;  // cols % 16 == 0: a block is all in or all out
+    const int64_t col = seg * kSegNv + lane * 8;
+    const bool cin = col < cols;  // cols % 16 == 0: a block (lane pair) is all in or all out
     constexpr int kR = kRowsNv / 4;  // rows per wave
 
     // issue this wave's loads first, then reduce the amax partials meanwhile
-    uint4 va[kR], vb[kR];
+    uint4 v[kR];
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = rb * kRowsNv + wave + 4 * i;
-        va[i] = vb[i] = make_uint4(0, 0, 0, 0);
-        if (cin && r < rows) {
-            va[i] = *reinterpret_cast<const uint4 *>(x + r * cols + col);
-            vb[i] = *reinterpret_cast<const uint4 *>(x + r * cols + col + 8);
-        }
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (cin && r < rows) v[i] = ld16<kNTLoadNvQuant>(x + r * cols + col);
     }
     uint32_t am = 0;
     for (int k = threadIdx.x; k < npartial; k += 256) am = max(am, partial[k]);
@@ -290,7 +293,8 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
     for (int i = 0; i < kR; ++i) {
         const int64_t r = rb * kRowsNv + wave + 4 * i;
         const bool ok = cin && r < rows;
-        const uint32_t b = max(amax8(va[i]), amax8(vb[i]));  // the block's amax
+        const uint32_t h = amax8(v[i]);
+        const uint32_t b = max(h, dpp_swap1(h));  // the block's amax (lane pair)
         uint32_t s;
         if (nonfinite) {
             s = 0x7Fu;
@@ -303,10 +307,12 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
         const float eff = e4m3_mag_value(s & 0x7Fu) * g;       // one IEEE fp32 multiplication
         const bool fast = !wave_any(nonfinite || !markstein_ok(eff));
         const float y = fast ? 1.0f / eff : 0.0f;
-        const uint2 codes = fast ? nvfp4_codes16(va[i], vb[i], eff, y, true, false)
-                                 : nvfp4_codes16(va[i], vb[i], eff, 0.0f, false, nonfinite);
+        const uint32_t codes = fast ? nvfp4_codes8(v[i], eff, y, true, false)
+                                    : nvfp4_codes8(v[i], eff, 0.0f, false, nonfinite);
         if (ok) {
-            st8<kNTStore>(q + r * (cols >> 1) + (col >> 1), codes);
+            st4<kNTStore>(q + r * (cols >> 1) + (col >> 1), codes);
+            // both lanes of the pair hold the same byte: storing it from each
+            // avoids an exec-mask change per row
             s_out[r * (cols >> 4) + (col >> 4)] = (uint8_t)s;
         }
     }
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__res
         pk[i] = 0u;
         eff[i] = 0.0f;
         if (r < rows) {
-            pk[i] = *reinterpret_cast<const uint32_t *>(q + r * (cols >> 1) + (col >> 1));
+            pk[i] = ld4<kNTLoadDq>(q + r * (cols >> 1) + (col >> 1));
             eff[i] = e4m3_to_f32(s_in[r * (cols >> 4) + (col >> 4)]) * g;  // one IEEE fp32 multiplication
         }
         bad |= !__builtin_isfinite(eff[i]);  // NaN products (x * NaN, 0 * Inf) take the sign rule
@@ -422,7 +428,7 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t nseg = (cols + kSegNv16 - 1) / kSegNv16;
+    const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
     const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,

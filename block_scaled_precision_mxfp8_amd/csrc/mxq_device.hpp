@@ -384,6 +384,23 @@ __device__ __forceinline__ uint4 ld16(const void *p)
 }
 
 template <bool kNT>
+__device__ __forceinline__ uint2 ld8(const void *p)
+{
+    if (kNT) {
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+        return make_uint2(v.x, v.y);
+    }
+    return *reinterpret_cast<const uint2 *>(p);
+}
+
+template <bool kNT>
+__device__ __forceinline__ uint32_t ld4(const void *p)
+{
+    if (kNT) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+    return *reinterpret_cast<const uint32_t *>(p);
+}
+
+template <bool kNT>
 __device__ __forceinline__ void st16(void *p, uint4 v)
 {
     if (kNT) {

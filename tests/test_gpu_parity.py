@@ -82,13 +82,15 @@ def test_rowwise_weight_4097_full(gpu, orc):
     check_rowwise(gpu, orc, workloads.weight_4097(), "weight_4097", fake_quant=False)
 
 
-def test_rowwise_strided_with_guard_bands(gpu, orc):
+@pytest.mark.parametrize("ldq", [104, 112])
+def test_rowwise_strided_with_guard_bands(gpu, orc, ldq):
     """Row strides beyond cols on input and outputs; 0xA5 guard bytes around
-    and between every output row must survive."""
-    rows, cols, ldx, ldq, lds, ldf = 37, 96, 128, 104, 5, 112
+    and between every output row must survive.  ldq 112 keeps code rows
+    16-byte aligned (paired 16-byte stores), 104 does not (8-byte stores)."""
+    rows, cols, ldx, lds, ldf = 37, 96, 128, 5, 112
     G = 256
     xb = workloads.random_bf16((rows, ldx), 77)
-    announce("rowwise strided/guard")
+    announce(f"rowwise strided/guard ldq={ldq}")
     xd = to_dev_bf16(xb)
     qbuf = torch.full((G + rows * ldq + G,), 0xA5, dtype=torch.uint8, device="cuda")
     sbuf = torch.full((G + rows * lds + G,), 0xA5, dtype=torch.uint8, device="cuda")
@@ -174,6 +176,42 @@ def test_colwise_edge_values(gpu, orc):
     xb[5, 7] = 0x7FC0
     xb[40, 9] = 0xFF80
     check_colwise(gpu, orc, xb, "colwise-edge")
+
+
+@pytest.mark.parametrize("offset", [0, 8])
+def test_colwise_output_alignment_with_guard_bands(gpu, orc, offset):
+    """Code outputs 16-byte aligned (paired 16-byte stores) or only 8-byte
+    aligned (8-byte stores), odd row count; guard bytes around each output
+    must survive."""
+    rows, cols, G = 37, 96, 256
+    xb = workloads.random_bf16((rows, cols), 4242)
+    announce(f"colwise alignment offset={offset}")
+    x = to_dev_bf16(xb)
+    ng = (rows + 31) // 32
+    bufs = {k: torch.full((2 * G + n,), 0xA5, dtype=torch.uint8, device="cuda")
+            for k, n in (("qc", rows * cols), ("sc", ng * cols), ("qr", rows * cols),
+                         ("sr", rows * cols // 32))}
+    fbuf = torch.full((2 * G + rows * cols,), 0x5A5A, dtype=torch.int16, device="cuda")
+    off = {"qc": G + offset, "sc": G, "qr": G + offset, "sr": G}
+    lib = gpu.load()
+    st = lib.mxq_quantize_colwise(
+        ctypes.c_void_p(x.data_ptr()), rows, cols,
+        *[ctypes.c_void_p(bufs[k].data_ptr() + off[k]) for k in ("qc", "sc", "qr", "sr")],
+        ctypes.c_void_p(fbuf.data_ptr() + 2 * G), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == mxq.MXQ_OK
+    torch.cuda.synchronize()
+    oqc, osc = orc.mxfp8_quantize_colwise(xb)
+    oqr, osr = orc.mxfp8_quantize_rowwise(xb)
+    want = {"qc": oqc, "sc": osc, "qr": oqr, "sr": osr}
+    for k, buf in bufs.items():
+        h = u8(buf)
+        n = want[k].size
+        assert np.all(h[:off[k]] == 0xA5) and np.all(h[off[k] + n:] == 0xA5), k
+        assert_same(f"aligned{offset} {k}", h[off[k]:off[k] + n].reshape(want[k].shape), want[k])
+    fh = fbuf.cpu().numpy().view(np.uint16)
+    assert np.all(fh[:G] == 0x5A5A) and np.all(fh[G + rows * cols:] == 0x5A5A)
+    assert_same(f"aligned{offset} fq", fh[G:G + rows * cols].reshape(rows, cols),
+                orc.mxfp8_dequantize(oqr, osr, 1))
 
 
 def test_colwise_act_16384_full(gpu, orc):
