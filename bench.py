@@ -359,7 +359,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "act_16384: bf16 [16384, 7168], 0.5*Student-t(3), seed 3; MXFP8 "
                                "column-wise + row-wise + fused row-wise fake-quant in one pass",
