@@ -2,7 +2,8 @@
 
 The C file ``mxq_oracle.c`` beside this module is the plain single-threaded
 definition of every output byte (MXFP8 row-/column-wise with pad-then-crop,
-dequantization and fake-quant, grouped row-wise, 128x128 block-FP8, NVFP4).
+dequantization and fake-quant, grouped row-wise, MXFP4, 128x128 block-FP8,
+NVFP4).
 This module only marshals numpy arrays into it through ctypes.
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
@@ -85,6 +86,12 @@ class Oracle:
         L.orc_mxfp8_dequantize.restype = None
         L.orc_mxfp8_fake_quant.argtypes = [_u16p, _i64, _i64, ctypes.c_int, _u16p]
         L.orc_mxfp8_fake_quant.restype = ctypes.c_int
+        L.orc_mxfp4_quantize.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
+        L.orc_mxfp4_quantize.restype = None
+        L.orc_mxfp4_dequantize.argtypes = [_u8p, _u8p, _i64, _i64, _u16p]
+        L.orc_mxfp4_dequantize.restype = None
+        L.orc_mxfp4_fake_quant.argtypes = [_u16p, _i64, _i64, _u16p]
+        L.orc_mxfp4_fake_quant.restype = ctypes.c_int
         L.orc_blockfp8_quantize.argtypes = [_u16p, _i64, _i64, ctypes.c_int32, _u8p, _f32p]
         L.orc_blockfp8_quantize.restype = None
         L.orc_blockfp8_dequantize.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int32, _u16p]
@@ -169,6 +176,34 @@ class Oracle:
     def mxfp8_quantize_rowwise_many(self, xs):
         """Independent row-wise quantization of each tensor, in order."""
         return [self.mxfp8_quantize_rowwise(x) for x in xs]
+
+    # ---- MXFP4 ------------------------------------------------------------
+    def mxfp4_quantize(self, x: np.ndarray):
+        """x: uint16 bf16 bits [rows, cols], cols % 32 == 0 ->
+        (q_packed [rows, cols/2] u8, scale [rows, cols/32] u8 E8M0)."""
+        x = _bits16(x)
+        rows, cols = x.shape
+        assert cols % 32 == 0
+        q = np.empty((rows, cols // 2), np.uint8)
+        s = np.empty((rows, cols // 32), np.uint8)
+        self.L.orc_mxfp4_quantize(_p(x, _u16p), rows, cols, _p(q, _u8p), _p(s, _u8p))
+        return q, s
+
+    def mxfp4_dequantize(self, q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        scale = np.ascontiguousarray(scale, dtype=np.uint8)
+        rows, cols = q.shape[0], 2 * q.shape[1]
+        out = np.empty((rows, cols), np.uint16)
+        self.L.orc_mxfp4_dequantize(_p(q, _u8p), _p(scale, _u8p), rows, cols, _p(out, _u16p))
+        return out
+
+    def mxfp4_fake_quant(self, x: np.ndarray) -> np.ndarray:
+        x = _bits16(x)
+        rows, cols = x.shape
+        out = np.empty((rows, cols), np.uint16)
+        rc = self.L.orc_mxfp4_fake_quant(_p(x, _u16p), rows, cols, _p(out, _u16p))
+        assert rc == 0
+        return out
 
     # ---- block-FP8 --------------------------------------------------------
     def blockfp8_quantize(self, x: np.ndarray, blk: int = 128):

@@ -42,7 +42,8 @@
  *                 E2M1 element {0, .5, 1, 1.5, 2, 3, 4, 6}; conversion to MX
  *                 takes the shared scale as the largest power of two <= amax
  *                 divided by the largest power of two of the element format
- *                 (2^8 for E4M3), and clamps elements to the max normal.
+ *                 (2^8 for E4M3, 2^2 for E2M1), and clamps elements to the
+ *                 max normal.
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes): RNE everywhere; saturation to the max finite value; the sign
@@ -317,6 +318,88 @@ void orc_mxfp8_quantize_rowwise_many(int32_t n, const uint16_t *const *xs,
 {
     for (int32_t t = 0; t < n; ++t)
         orc_mxfp8_quantize_rowwise(xs[t], rows[t], cols[t], qs[t], ss[t]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4: groups of 32, one E8M0 scale, E2M1 elements [V4-mxfp4]             */
+/* ------------------------------------------------------------------------ */
+
+/* Shared scale byte [OCP-MX]: 2^(floor(log2 amax) - 2) -- 4 = 2^2 is E2M1's
+ * largest power of two -- as an E8M0 byte clamped at 0 (2^-127); an all-zero
+ * group gets 0; a group holding NaN or Inf gets 0xFF. */
+static uint8_t mx4_scale_byte(const double *vals, int n)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double a = fabs(vals[i]);
+        if (!isfinite(a)) return 0xFF;
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0) return 0;
+    int E = floor_log2(amax) - 2;           /* 2 = exponent of 4, E2M1's largest power of two */
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
+    return (uint8_t)(E + 127);
+}
+
+/* Row-wise MXFP4 (the simulate-QAT groups of 32 along the last dimension
+ * [V4-mxfp4]): x [rows, cols] bf16, cols % 32 == 0.  Element nibble =
+ * E2M1(x / 2^(s-127)) (exact quotient, RNE, saturating at +-6, sign kept);
+ * a NaN group (scale 0xFF) has nibbles 0x7 | sign, E2M1 having no NaN.
+ * q [rows, cols/2]: element 2j in the low nibble of byte j, element 2j+1 in
+ * the high nibble (`float4_e2m1fn_x2`); scale [rows, cols/32] E8M0. */
+void orc_mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                        uint8_t *scale)
+{
+    double g[MX_GROUP];
+    uint8_t nib[MX_GROUP];
+    int64_t ng = cols / MX_GROUP;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t k = 0; k < ng; ++k) {
+            const uint16_t *src = x + r * cols + k * MX_GROUP;
+            for (int i = 0; i < MX_GROUP; ++i) g[i] = orc_bf16_to_double(src[i]);
+            uint8_t s = mx4_scale_byte(g, MX_GROUP);
+            scale[r * ng + k] = s;
+            for (int i = 0; i < MX_GROUP; ++i)
+                nib[i] = s == 0xFF ? (uint8_t)((signbit(g[i]) ? 0x8 : 0) | 0x7)
+                                   : orc_double_to_e2m1(ldexp(g[i], 127 - (int)s));
+            for (int i = 0; i < MX_GROUP; i += 2)
+                q[r * (cols / 2) + (k * MX_GROUP + i) / 2] = (uint8_t)(nib[i] | (nib[i + 1] << 4));
+        }
+    }
+}
+
+/* MXFP4 dequantization: bf16_RNE(E2M1(nibble) * 2^(s-127)), the product exact
+ * in double; scale 0xFF gives the quiet NaN with the nibble's sign. */
+void orc_mxfp4_dequantize(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
+                          uint16_t *out)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            uint8_t byte = q[r * (cols / 2) + c / 2];
+            uint8_t nib = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+            uint8_t s = scale[r * (cols / MX_GROUP) + c / MX_GROUP];
+            uint16_t o;
+            if (s == 0xFF)
+                o = (uint16_t)((nib & 0x8) ? 0xFFC0 : 0x7FC0);
+            else
+                o = orc_double_to_bf16(orc_e2m1_to_double(nib) * orc_e8m0_to_double(s));
+            out[r * cols + c] = o;
+        }
+    }
+}
+
+/* MXFP4 fake quantization (`mxfp4_simulate_qat(x, 32)` [V4-mxfp4, compressor
+ * review]): quantize row-wise, then dequantize back to bf16. */
+int orc_mxfp4_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, uint16_t *out)
+{
+    uint8_t *q = (uint8_t *)malloc((size_t)(rows * cols / 2));
+    uint8_t *s = (uint8_t *)malloc((size_t)(rows * (cols / MX_GROUP)));
+    if (!q || !s) { free(q); free(s); return -1; }
+    orc_mxfp4_quantize(x, rows, cols, q, s);
+    orc_mxfp4_dequantize(q, s, rows, cols, out);
+    free(q); free(s);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */

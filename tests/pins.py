@@ -434,3 +434,143 @@ def pin_nvfp4(orc, x):
     sv = torch.from_numpy(s.copy()).view(torch.float8_e4m3fn).float() * float(g[0])
     ref = (ev * sv.repeat_interleave(16, dim=1)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(dq, ref)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 pins
+# ---------------------------------------------------------------------------
+
+def unpack_nibbles(q: np.ndarray) -> np.ndarray:
+    """[rows, cols/2] packed bytes -> [rows, cols] nibbles, element 2j from the
+    low nibble of byte j."""
+    n = np.empty((q.shape[0], 2 * q.shape[1]), np.int64)
+    n[:, 0::2] = q & 0xF
+    n[:, 1::2] = q >> 4
+    return n
+
+
+def mx4_scale_closed_form(group_bits: np.ndarray) -> np.ndarray:
+    """E8M0 byte straight from bf16 bits: max(expfield(max magnitude) - 2, 0);
+    0xFF when the group holds Inf/NaN."""
+    mag = (group_bits.astype(np.int64) & 0x7FFF).max(axis=-1)
+    e = mag >> 7
+    return np.where(e == 0xFF, 0xFF, np.maximum(e - 2, 0))
+
+
+def mx4_sweep_input(scale_bytes=range(0, 253)):
+    """Every bf16 magnitude (both signs) that can share a group with scale byte
+    s: groups of 31 test values plus one anchor whose exponent field is s + 2
+    (mantissa all ones, so it is the group's amax)."""
+    groups, expect_s = [], []
+    for s in scale_bytes:
+        e_anchor = s + 2 if s > 0 else 2
+        anchor = (e_anchor << 7) | 0x7F
+        mags = np.arange(0, anchor + 1, dtype=np.uint32)
+        vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+        pad = (-len(vals)) % 31
+        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 31)
+        g = np.concatenate([np.full((len(vals), 1), anchor, np.uint16), vals], axis=1)
+        groups.append(g)
+        expect_s.append(np.full(len(g), s))
+    return np.concatenate(groups), np.concatenate(expect_s)
+
+
+def pin_mx4_sweep(orc, scale_bytes=range(0, 253)):
+    """MXFP4 over every (bf16 value, reachable scale byte) pair vs the closed-form
+    scale and an exhaustive nearest search over the E2M1 values of x / 2^(s-127)."""
+    x, s_exp = mx4_sweep_input(scale_bytes)
+    q, s = orc.mxfp4_quantize(x)
+    assert np.array_equal(s[:, 0].astype(np.int64), s_exp)
+    assert np.array_equal(mx4_scale_closed_form(x), s_exp)
+    v = torch_bf16_values(x) * np.exp2(127.0 - s_exp)[:, None]  # exact power-of-two shift
+    ref = nearest_code(v.ravel(), E2M1_POS, 0x8).reshape(v.shape)
+    assert np.array_equal(unpack_nibbles(q), ref)
+
+
+def pin_mx4_nonfinite(orc):
+    x = np.zeros((3, 64), np.uint16)
+    x[0, :32] = np.arange(32, dtype=np.uint16) | 0x3F00
+    x[0, 5] = 0x7FC0                       # NaN in group 0
+    x[1, 40] = 0xFF80                      # -Inf in group 1
+    x[1, 41] = 0xBF80                      # -1 beside it
+    x[2, :] = 0x3F80                       # 1.0: byte floor(log2 1) - 2 + 127 = 125, nibble 4 -> 0x6
+    q, s = orc.mxfp4_quantize(x)
+    n = unpack_nibbles(q)
+    assert s[0, 0] == 0xFF and s[1, 1] == 0xFF and s[0, 1] == 0 and s[1, 0] == 0
+    assert np.all(n[0, :32] == 0x7)
+    assert n[1, 40] == 0xF and n[1, 41] == 0xF and n[1, 42] == 0x7
+    assert np.all(s[2] == 125) and np.all(n[2] == 0x6)
+    # packing: element 2j in the low nibble (1.0 and 4.0 with scale 1 -> 0x62)
+    y = np.zeros((1, 32), np.uint16)
+    y[0, 0], y[0, 1] = 0x3F80, 0x4080
+    qy, sy = orc.mxfp4_quantize(y)
+    assert sy[0, 0] == 127 and qy[0, 0] == 0x62 and np.all(qy[0, 1:] == 0)
+
+
+def pin_mx4_edge_groups(orc, x=None):
+    import workloads
+    if x is None:
+        x = workloads.mx_small()
+    q, s = orc.mxfp4_quantize(x)
+    n = unpack_nibbles(q)
+    for kind, r, c, want in read_golden("mxfp4_small_edge_groups.txt"):
+        r, c, want = int(r), int(c), int(want, 16)
+        if kind == "scale":
+            assert s[r, c] == want, (r, c)
+        elif kind == "allb":
+            assert np.all(q[r, 16 * c:16 * c + 16] == want), (r, c)
+        else:
+            assert n[r, c] == want, (r, c)
+    assert np.array_equal(s.astype(np.int64), mx4_scale_closed_form(x.reshape(x.shape[0], -1, 32)))
+
+
+def pin_mx4_max_nibble(orc, x):
+    """Scale exponent floor(log2 amax) - 2 puts the group max in [4, 8) before
+    rounding, so its nibble magnitude is 0x6 (4) or 0x7 (6) unless the scale
+    byte is clamped at 0."""
+    q, s = orc.mxfp4_quantize(x)
+    mag = (unpack_nibbles(q).reshape(x.shape[0], -1, 32) & 0x7).max(axis=-1)
+    unclamped = (mx4_scale_closed_form(x.reshape(x.shape[0], -1, 32)) > 0) & (s != 0xFF)
+    assert np.all((mag[unclamped] == 0x6) | (mag[unclamped] == 0x7))
+
+
+def pin_mx4_dequant_vs_torch(orc):
+    """Every (nibble, scale byte) pair: bf16 RNE of E2M1 value * 2^(b-127) via
+    torch's fp32 product and cast (exact here, subnormals kept)."""
+    nib = np.tile(np.arange(16, dtype=np.uint8), (256, 2))              # [256, 32] nibbles
+    q = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)          # [256, 16] packed
+    sc = np.arange(256, dtype=np.uint8)[:, None].copy()                 # one group per row
+    out = orc.mxfp4_dequantize(q, sc)
+    ev = np.where(nib >= 8, -E2M1_POS[nib & 7], E2M1_POS[nib & 7]).astype(np.float32)
+    e = np.arange(256.0)
+    e[255] = 127.0
+    X = np.exp2(e - 127.0).astype(np.float32)[:, None]
+    with np.errstate(over="ignore"):   # 6 * 2^127 overflows to Inf, as bf16 RNE does
+        ref = torch.from_numpy(ev * X).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out[:255], ref[:255])
+    assert np.array_equal(out[255], np.where(nib[255] >= 8, 0xFFC0, 0x7FC0).astype(np.uint16))
+
+
+def pin_mx4_roundtrip(orc, x):
+    """Idempotence q(dq(q(x))) == q(x) (E2M1 times a power of two is exact in
+    bf16, so dq re-quantizes to itself) and the round-trip bound: |dq - x| <=
+    half an E2M1 ulp of x/X (0.5 below 2, 1 below 4, 2 up to 6), times X,
+    unless x/X > 6 (saturated: |dq - x| = |x| - 6 X); fake-quant equals
+    dequantize(quantize(x))."""
+    q, s = orc.mxfp4_quantize(x)
+    dq = orc.mxfp4_dequantize(q, s)
+    assert np.array_equal(orc.mxfp4_fake_quant(x), dq)
+    fin_g = s != 0xFF
+    q2, s2 = orc.mxfp4_quantize(dq)
+    fm = np.repeat(fin_g, 16, axis=1)
+    assert np.array_equal(s[fin_g], s2[fin_g]) and np.array_equal(q[fm], q2[fm])
+    xv = torch_bf16_values(x)
+    dv = torch_bf16_values(dq)
+    X = np.repeat(np.exp2(s.astype(np.float64) - 127.0), 32, axis=1)
+    t = np.abs(xv) / X
+    half_ulp = np.where(t < 2, 0.25, np.where(t < 4, 0.5, 1.0)) * X
+    sat = t > 6
+    fin = np.isfinite(xv) & np.repeat(fin_g, 32, axis=1)
+    err = np.abs(dv - xv)
+    assert np.all(err[fin & ~sat] <= half_ulp[fin & ~sat])
+    assert np.array_equal(err[fin & sat], (np.abs(xv) - 6 * X)[fin & sat])

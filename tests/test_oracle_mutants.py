@@ -10,9 +10,16 @@ import workloads
 # (name, exact text in the oracle source, replacement)
 MUTANTS = [
     ("scale exponent off by one", "floor_log2(amax) - 8;", "floor_log2(amax) - 7;"),
-    ("scale clamp at 2^-126", "if (E < -127) E = -127;", "if (E < -126) E = -126;"),
-    ("zero group scale 1.0", "if (amax == 0.0) return 0;", "if (amax == 0.0) return 127;"),
-    ("Inf not a NaN group", "if (!isfinite(a)) return 0xFF;", "if (isnan(a)) return 0xFF;"),
+    ("scale clamp at 2^-126", "E4M3's largest power of two */\n    if (E < -127) E = -127;",
+     "E4M3's largest power of two */\n    if (E < -126) E = -126;"),
+    ("zero group scale 1.0", "if (amax == 0.0) return 0;\n    int E = floor_log2(amax) - 8;",
+     "if (amax == 0.0) return 127;\n    int E = floor_log2(amax) - 8;"),
+    ("Inf not a NaN group",
+     "mx_scale_byte(const double *vals, int n)\n{\n    double amax = 0.0;\n    for (int i = 0; i < n; ++i) {\n        double a = fabs(vals[i]);\n        if (!isfinite(a)) return 0xFF;",
+     "mx_scale_byte(const double *vals, int n)\n{\n    double amax = 0.0;\n    for (int i = 0; i < n; ++i) {\n        double a = fabs(vals[i]);\n        if (isnan(a)) return 0xFF;"),
+    ("mxfp4 Inf not a NaN group",
+     "mx4_scale_byte(const double *vals, int n)\n{\n    double amax = 0.0;\n    for (int i = 0; i < n; ++i) {\n        double a = fabs(vals[i]);\n        if (!isfinite(a)) return 0xFF;",
+     "mx4_scale_byte(const double *vals, int n)\n{\n    double amax = 0.0;\n    for (int i = 0; i < n; ++i) {\n        double a = fabs(vals[i]);\n        if (isnan(a)) return 0xFF;"),
     ("E4M3 ties away from zero",
      "double quantum = ldexp(1.0, E - 3);     /* 3 fraction bits */\n    double n = nearbyint(a / quantum);",
      "double quantum = ldexp(1.0, E - 3);     /* 3 fraction bits */\n    double n = round(a / quantum);"),
@@ -21,8 +28,10 @@ MUTANTS = [
     ("E4M3 drops sign of small codes", "if (r < ldexp(1.0, -6)) return sign | (uint8_t)n;",
      "if (r < ldexp(1.0, -6)) return (uint8_t)n;"),
     ("bf16 rounding flushes subnormals", "if (E < -126) E = -126;", "if (E < -126) return sign;"),
-    ("dequant scale index", "scale[r * (cols / MX_GROUP) + c / MX_GROUP]",
-     "scale[r * (cols / MX_GROUP) + (c % (cols / MX_GROUP))]"),
+    ("dequant scale index", "axis == 1 ? scale[r * (cols / MX_GROUP) + c / MX_GROUP]",
+     "axis == 1 ? scale[r * (cols / MX_GROUP) + (c % (cols / MX_GROUP))]"),
+    ("mxfp4 dequant scale index", "uint8_t s = scale[r * (cols / MX_GROUP) + c / MX_GROUP];",
+     "uint8_t s = scale[r * (cols / MX_GROUP) + (c % (cols / MX_GROUP))];"),
     ("colwise scale transposed", "scale[j * cols + c] = s;", "scale[c * nrg + j] = s;"),
     ("colwise group stride", "q[(r0 + i) * cols + c] = mx_encode(g[i], s);",
      "q[(r0 + i) * cols + c] = mx_encode(g[i], (uint8_t)(s + (i == 31)));"),
@@ -30,7 +39,19 @@ MUTANTS = [
     ("blockfp8 zero tile unguarded", "divisor = (amax == 0.0) ? 1.0f : S;", "divisor = S;"),
     ("blockfp8 reciprocal multiply", "float t = xf / divisor;", "float t = xf * (1.0f / divisor);"),
     ("nvfp4 global 2687", "float g = (float)A / 2688.0f;", "float g = (float)A / 2687.0f;"),
-    ("nvfp4 nibble order", "(uint8_t)(nib[i] | (nib[i + 1] << 4));", "(uint8_t)(nib[i + 1] | (nib[i] << 4));"),
+    ("nvfp4 nibble order", "                    (uint8_t)(nib[i] | (nib[i + 1] << 4));",
+     "                    (uint8_t)(nib[i + 1] | (nib[i] << 4));"),
+    ("mxfp4 scale exponent -1", "int E = floor_log2(amax) - 2;", "int E = floor_log2(amax) - 1;"),
+    ("mxfp4 nibble order", "/ 2] = (uint8_t)(nib[i] | (nib[i + 1] << 4));",
+     "/ 2] = (uint8_t)(nib[i + 1] | (nib[i] << 4));"),
+    ("mxfp4 NaN group nibble", "? (uint8_t)((signbit(g[i]) ? 0x8 : 0) | 0x7)",
+     "? (uint8_t)((signbit(g[i]) ? 0x8 : 0) | 0x6)"),
+    ("mxfp4 dequant reads the high nibble first", "(c % 2 == 0) ? (byte & 0xF) : (byte >> 4);",
+     "(c % 2 == 0) ? (byte >> 4) : (byte & 0xF);"),
+    ("mxfp4 scale clamp at 2^-126", "E2M1's largest power of two */\n    if (E < -127) E = -127;",
+     "E2M1's largest power of two */\n    if (E < -126) E = -126;"),
+    ("mxfp4 zero group scale 1.0", "if (amax == 0.0) return 0;\n    int E = floor_log2(amax) - 2;",
+     "if (amax == 0.0) return 127;\n    int E = floor_log2(amax) - 2;"),
     ("nvfp4 eff divides", "float eff = (float)orc_e4m3_to_double(s) * g;",
      "float eff = (float)orc_e4m3_to_double(s) / g;"),
     ("nvfp4 block scale without 6", "float d = 6.0f * g;", "float d = 4.0f * g;"),
@@ -64,6 +85,12 @@ def all_pins(orc):
     z[:, :128] = 0
     pins.pin_blockfp8(orc, z, 128)
     pins.pin_nvfp4(orc, workloads.random_bf16((64, 256), 21))
+    pins.pin_mx4_sweep(orc, scale_bytes=list(range(0, 20)) + list(range(20, 253, 13)))
+    pins.pin_mx4_nonfinite(orc)
+    pins.pin_mx4_edge_groups(orc)
+    pins.pin_mx4_max_nibble(orc, x)
+    pins.pin_mx4_dequant_vs_torch(orc)
+    pins.pin_mx4_roundtrip(orc, workloads.mx_small())
 
 
 def test_unmutated_source_passes_all_pins(tmp_path):

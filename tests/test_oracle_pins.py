@@ -140,3 +140,39 @@ def test_blockfp8_nonfinite_tile(orc):
     q, S = orc.blockfp8_quantize(x, 128)
     assert np.isnan(S[0, 0]) and np.isfinite(S[0, 1])
     assert np.all((q[:, :128] & 0x7F) == 0x7F)
+
+
+def test_mx4_sweep_every_value_every_scale(orc):
+    """All (bf16 value, reachable scale byte) pairs through MXFP4."""
+    pins.pin_mx4_sweep(orc)
+
+
+def test_mx4_nonfinite_groups_and_packing(orc):
+    pins.pin_mx4_nonfinite(orc)
+
+
+def test_mx4_small_edge_groups(orc):
+    pins.pin_mx4_edge_groups(orc)
+
+
+@pytest.mark.parametrize("which", ["normal", "t3", "weight"])
+def test_mx4_max_nibble(orc, which):
+    x = {"normal": lambda: workloads.random_bf16((97, 1024), 13),
+         "t3": lambda: workloads.act_16384(rows=64),
+         "weight": lambda: np.ascontiguousarray(workloads.weight_4097()[:128])}[which]()
+    pins.pin_mx4_max_nibble(orc, x)
+
+
+def test_mx4_dequant_all_nibbles_all_scales(orc):
+    pins.pin_mx4_dequant_vs_torch(orc)
+
+
+@pytest.mark.parametrize("which", ["mx_small", "t3", "weight"])
+def test_mx4_roundtrip_and_idempotence(orc, which):
+    if which == "mx_small":
+        x = workloads.mx_small()
+    elif which == "t3":
+        x = workloads.act_16384(rows=128)
+    else:
+        x = workloads.weight_4097()[:256]
+    pins.pin_mx4_roundtrip(orc, np.ascontiguousarray(x))
