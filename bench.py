@@ -129,7 +129,9 @@ def main():
                 "sc": torch.empty(((rows + 31) // 32, cols), dtype=torch.uint8, device=dev),
                 "qr": torch.empty((rows, cols), dtype=torch.uint8, device=dev),
                 "sr": torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
-                "fq": torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)}
+                "fq": torch.empty((rows, cols), dtype=torch.bfloat16, device=dev),
+                "q4": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                "s4": torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)}
 
     batches = [batch(x0) for _ in range(BATCHES)]
     del x0
@@ -258,6 +260,18 @@ def main():
         breakdown["act_16384 fake-quant only"] = rotated(
             [lambda d=d: check(lib.mxq_fake_quant(P(d["x"]), rows, cols, 1, P(d["fq"]), sp),
                                "fake_quant") for d in batches], 4 * e)
+        # MXFP4 on the same batches: quantize, simulate-QAT, dequantize
+        m4 = 2 * e + e // 2 + e // 32
+        breakdown["act_16384 MXFP4 quantize"] = rotated(
+            [lambda d=d: check(lib.mxfp4_quantize(P(d["x"]), rows, cols, P(d["q4"]), P(d["s4"]),
+                                                  None, sp), "mxfp4") for d in batches], m4)
+        breakdown["act_16384 MXFP4 simulate-QAT (fake-quant only)"] = rotated(
+            [lambda d=d: check(lib.mxfp4_fake_quant(P(d["x"]), rows, cols, P(d["fq"]), sp),
+                               "mxfp4 fq") for d in batches], 4 * e)
+        breakdown["act_16384 MXFP4 dequantize"] = rotated(
+            [lambda d=d: check(lib.mxfp4_dequantize(P(d["q4"]), P(d["s4"]), rows, cols, P(d["fq"]),
+                                                    sp), "mxfp4 dq") for d in batches],
+            e // 2 + e // 32 + 2 * e)
         del batches
         torch.cuda.empty_cache()
 

@@ -51,6 +51,9 @@ SIGNATURES = {
     "mxq_quantize_rowwise_grouped": (ctypes.c_int, [_vp, _i32, _vp, _sz, _vp]),
     "blockfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "blockfp8_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "mxfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "mxfp4_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "mxfp4_fake_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "nvfp4_workspace_size": (_sz, []),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
@@ -256,6 +259,46 @@ def blockfp8_dequantize(q: torch.Tensor, S: torch.Tensor, blk: int = 128) -> tor
                                     _ptr(out), _stream(q))
     _check("blockfp8_dequantize", st)
     return out
+
+
+def mxfp4_quantize(x: torch.Tensor, fake_quant: bool = False):
+    """MXFP4 of a [..., cols] bf16 tensor flattened to 2-D: (q uint8 [rows,
+    cols/2] packed E2M1, scale uint8 [rows, cols/32] E8M0) and, with
+    fake_quant, the bf16 dequantization of that result as a third tensor."""
+    _need_bf16_cuda(x)
+    x = _as_2d_rows(x).contiguous()
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows, cols // MX_GROUP if cols % MX_GROUP == 0 else 0), dtype=torch.uint8,
+                    device=dev)
+    fq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if fake_quant else None
+    st = load().mxfp4_quantize(_ptr(x), rows, cols, _ptr(q), _ptr(s), _ptr(fq), _stream(x))
+    _check("mxfp4_quantize", st)
+    return (q, s, fq) if fake_quant else (q, s)
+
+
+def mxfp4_dequantize(q: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    q = q.contiguous()
+    scale = scale.contiguous()
+    rows, cols = q.shape[0], 2 * q.shape[1]
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=q.device)
+    st = load().mxfp4_dequantize(_ptr(q.view(torch.uint8)), _ptr(scale.view(torch.uint8)), rows,
+                                 cols, _ptr(out), _stream(q))
+    _check("mxfp4_dequantize", st)
+    return out
+
+
+def mxfp4_simulate_qat(x: torch.Tensor) -> torch.Tensor:
+    """MXFP4 fake quantization (groups of 32 along the last dimension) of a
+    [..., cols] bf16 tensor: bf16 of the same shape."""
+    _need_bf16_cuda(x)
+    x2 = _as_2d_rows(x).contiguous()
+    rows, cols = x2.shape
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x2.device)
+    st = load().mxfp4_fake_quant(_ptr(x2), rows, cols, _ptr(out), _stream(x2))
+    _check("mxfp4_fake_quant", st)
+    return out.view(x.shape)
 
 
 def nvfp4_workspace(device) -> torch.Tensor:

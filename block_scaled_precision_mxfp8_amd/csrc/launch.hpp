@@ -36,6 +36,11 @@ hipError_t launch_mx_grouped(const GroupEntry *table_dev, const int32_t *starts_
 
 int64_t mx_row_tiles(int64_t rows, int64_t cols, int64_t *nseg);
 
+hipError_t launch_mx4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                            uint8_t *scale, uint16_t *fq, hipStream_t stream);
+hipError_t launch_mx4_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
+                              uint16_t *out, hipStream_t stream);
+
 hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
                              float *scale, hipStream_t stream);
 hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,

@@ -132,6 +132,42 @@ mxq_status mxq_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, int axi
     return from_hip(e);
 }
 
+mxq_status mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
+                          uint8_t *scale, uint16_t *fq, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !q_packed || !scale) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(q_packed, 4) || (fq && !aligned(fq, 16))) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_mx4_quant(x, rows, cols, q_packed, scale, fq, as_stream(stream)));
+}
+
+mxq_status mxfp4_dequantize(const uint8_t *q_packed, const uint8_t *scale, int64_t rows,
+                            int64_t cols, uint16_t *out, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!q_packed || !scale || !out) return MXQ_EINVAL;
+    if (!aligned(q_packed, 4) || !aligned(out, 16)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_mx4_dequant(q_packed, scale, rows, cols, out, as_stream(stream)));
+}
+
+mxq_status mxfp4_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, uint16_t *out,
+                            void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !out) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(out, 16)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_mx4_quant(x, rows, cols, nullptr, nullptr, out, as_stream(stream)));
+}
+
 size_t mxq_grouped_workspace_size(int32_t n)
 {
     // [GroupEntry x n][int32 first tile x n], rounded up to 16 bytes

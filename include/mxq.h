@@ -15,6 +15,8 @@
  *     saturate at +-448.
  *   - Fake quantization (quantize, then dequantize back to bf16) for
  *     simulated QAT: miles PR #1372 "V4 mxfp4", the compressor review.
+ *   - MXFP4 (the same groups of 32 and E8M0 scales, E2M1 elements packed two
+ *     per byte) and its simulate-QAT fake quantization: the same page.
  *   - Block-FP8 (128 x 128 absmax, fp32 scale) and NVFP4 (global fp32 scale x
  *     per-16 E4M3 scale, E2M1 elements packed two per byte): xorl PR #30 "Add
  *     FP8, NVFP4, and QARL training and export", deep review, "What looked
@@ -167,6 +169,39 @@ mxq_status blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int3
  * gives the quiet NaN with the code's sign.  Same shapes and rules as above. */
 mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
                                int32_t blk, uint16_t *out, void *stream);
+
+/*
+ * MXFP4 quantization (miles PR #1372 "V4 mxfp4": mxfp4_simulate_qat with
+ * groups of 32 in the compressor review; the packed [..., N/2] FP4 output in
+ * the review of fp4_act_quant).  Every 32 consecutive values of a row share
+ * one E8M0 scale byte floor(log2 amax) - 2 + 127, clamped at 0 (the OCP
+ * microscaling conversion for E2M1, whose largest power of two is 2^2); 0
+ * for an all-zero group, 0xFF for a group holding NaN or Inf.  Elements are
+ * E2M1 nibbles of x / 2^(byte - 127), round to nearest even, saturating at
+ * +-6, sign kept (a NaN group: 0x7 with each element's sign).
+ *   x          [rows, cols] bf16, contiguous, 16-byte aligned
+ *   q_packed   [rows, cols/2] bytes, contiguous, 4-byte aligned; element 2j
+ *              in the low nibble of byte j, 2j+1 in the high nibble
+ *   scale      [rows, cols/32] E8M0 bytes, contiguous
+ *   fq         optional [rows, cols] bf16 = mxfp4_dequantize(q_packed,
+ *              scale), contiguous, 16-byte aligned; NULL to skip
+ * Shape: cols % 32 == 0 (MXQ_ESHAPE otherwise); any rows >= 0.
+ */
+mxq_status mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
+                          uint8_t *scale, uint16_t *fq, void *stream);
+
+/* MXFP4 dequantization: out = bf16(E2M1(nibble) * 2^(byte - 127)), exact (the
+ * value has two significant bits and the scale is at least 2^-127) or +-Inf
+ * when it overflows bf16; scale byte 0xFF gives the quiet NaN with the
+ * nibble's sign.  Shapes as mxfp4_quantize; out 16-byte aligned. */
+mxq_status mxfp4_dequantize(const uint8_t *q_packed, const uint8_t *scale, int64_t rows,
+                            int64_t cols, uint16_t *out, void *stream);
+
+/* MXFP4 fake quantization, mxfp4_simulate_qat(x, 32): out =
+ * mxfp4_dequantize(mxfp4_quantize(x)) in one pass, without writing codes or
+ * scales.  x and out [rows, cols] bf16, contiguous, 16-byte aligned. */
+mxq_status mxfp4_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, uint16_t *out,
+                            void *stream);
 
 /*
  * NVFP4 two-level quantization (xorl PR #30, "What looked solid":

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "mxq.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = set(re.findall(r"\b((?:mxq|blockfp8|nvfp4)_\w+)\s*\(", text))
+    names = set(re.findall(r"\b((?:mxq|blockfp8|nvfp4|mxfp4)_\w+)\s*\(", text))
     return sorted(names)
 
 
@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     for want in ["mxq_quantize_rowwise", "mxq_quantize_colwise", "mxq_dequantize", "mxq_fake_quant",
                  "mxq_quantize_rowwise_grouped", "blockfp8_quantize", "blockfp8_dequantize",
                  "nvfp4_quantize", "nvfp4_dequantize", "mxq_status_string", "mxq_abi_version",
-                 "mxq_grouped_workspace_size", "nvfp4_workspace_size"]:
+                 "mxq_grouped_workspace_size", "nvfp4_workspace_size", "mxfp4_quantize",
+                 "mxfp4_dequantize", "mxfp4_fake_quant"]:
         assert want in names
     assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
 
@@ -150,11 +151,36 @@ def test_blockfp8_nvfp4_errors(lib):
     assert nd(NULL, NULL, NULL, 0, 32, NULL, NULL) == mxq.MXQ_OK
 
 
+def test_mxfp4_errors(lib):
+    f = lib.mxfp4_quantize
+    assert f(P16, -1, 32, P16, P16, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 48, P16, P16, NULL, NULL) == mxq.MXQ_ESHAPE                 # cols % 32
+    assert f(NULL, 4, 32, P16, P16, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, NULL, P16, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, P16, NULL, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P8, 4, 32, P16, P16, NULL, NULL) == mxq.MXQ_EALIGN                  # x 16-aligned
+    assert f(P16, 4, 32, P2, P16, NULL, NULL) == mxq.MXQ_EALIGN                  # q 4-aligned
+    assert f(P16, 4, 32, P16, P16, P8, NULL) == mxq.MXQ_EALIGN                   # fq 16-aligned
+    assert f(P16, 2**62, 64, P16, P16, NULL, NULL) == mxq.MXQ_ESIZE
+    assert f(NULL, 0, 32, NULL, NULL, NULL, NULL) == mxq.MXQ_OK
+    d = lib.mxfp4_dequantize
+    assert d(P16, P16, 4, 40, P16, NULL) == mxq.MXQ_ESHAPE
+    assert d(P16, NULL, 4, 32, P16, NULL) == mxq.MXQ_EINVAL
+    assert d(P2, P16, 4, 32, P16, NULL) == mxq.MXQ_EALIGN
+    assert d(P16, P16, 4, 32, P8, NULL) == mxq.MXQ_EALIGN
+    assert d(NULL, NULL, 0, 32, NULL, NULL) == mxq.MXQ_OK
+    fq = lib.mxfp4_fake_quant
+    assert fq(P16, 4, 33, P16, NULL) == mxq.MXQ_ESHAPE
+    assert fq(P16, 4, 32, NULL, NULL) == mxq.MXQ_EINVAL
+    assert fq(P2, 4, 32, P16, NULL) == mxq.MXQ_EALIGN
+    assert fq(P16, -4, 32, P16, NULL) == mxq.MXQ_EINVAL
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((4, 32), dtype=torch.bfloat16)
     for fn in (mxq.quantize_rowwise, mxq.fake_quant, mxq.blockfp8_quantize, mxq.nvfp4_quantize,
-               mxq.mxfp8_quantize):
+               mxq.mxfp8_quantize, mxq.mxfp4_quantize, mxq.mxfp4_simulate_qat):
         with pytest.raises(ValueError):
             fn(x)
     with pytest.raises(TypeError):
