@@ -82,6 +82,8 @@ class Oracle:
         L.orc_mxfp8_quantize_padcrop.restype = ctypes.c_int
         L.orc_mxfp8_quantize_colwise.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
         L.orc_mxfp8_quantize_colwise.restype = None
+        L.orc_mxfp8_quantize_colwise_t.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
+        L.orc_mxfp8_quantize_colwise_t.restype = ctypes.c_int
         L.orc_mxfp8_dequantize.argtypes = [_u8p, _u8p, _i64, _i64, ctypes.c_int, _u16p]
         L.orc_mxfp8_dequantize.restype = None
         L.orc_mxfp8_fake_quant.argtypes = [_u16p, _i64, _i64, ctypes.c_int, _u16p]
@@ -155,6 +157,18 @@ class Oracle:
         s = np.empty(((rows + 31) // 32, cols), np.uint8)
         self.L.orc_mxfp8_quantize_colwise(_p(x, _u16p), rows, cols, _p(q, _u8p), _p(s, _u8p))
         return q, s
+
+    def mxfp8_quantize_colwise_t(self, x: np.ndarray):
+        """-> (qt [cols, rows] u8: codes of the column groups, transposed;
+        st [cols, ceil(rows/32)] u8)."""
+        x = _bits16(x)
+        rows, cols = x.shape
+        qt = np.empty((cols, rows), np.uint8)
+        st = np.empty((cols, (rows + 31) // 32), np.uint8)
+        rc = self.L.orc_mxfp8_quantize_colwise_t(_p(x, _u16p), rows, cols, _p(qt, _u8p),
+                                                 _p(st, _u8p))
+        assert rc == 0
+        return qt, st
 
     def mxfp8_dequantize(self, q: np.ndarray, scale: np.ndarray, axis: int = 1) -> np.ndarray:
         q = np.ascontiguousarray(q, dtype=np.uint8)

@@ -272,6 +272,26 @@ void orc_mxfp8_quantize_colwise(const uint16_t *x, int64_t rows, int64_t cols,
     }
 }
 
+/* Column-wise MXFP8 in the transposed layout a backward-pass GEMM reads: the
+ * groups and codes of orc_mxfp8_quantize_colwise, stored as qt [cols, rows]
+ * (qt[c * rows + r] is the code of x[r, c]) and st [cols, ceil(rows/32)]
+ * (st[c * ceil(rows/32) + j] is the scale of rows 32j.. of column c). */
+int orc_mxfp8_quantize_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qt,
+                                 uint8_t *st)
+{
+    int64_t nrg = (rows + MX_GROUP - 1) / MX_GROUP;
+    uint8_t *q = (uint8_t *)malloc((size_t)(rows * cols));
+    uint8_t *s = (uint8_t *)malloc((size_t)(nrg * cols));
+    if (!q || !s) { free(q); free(s); return -1; }
+    orc_mxfp8_quantize_colwise(x, rows, cols, q, s);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) qt[c * rows + r] = q[r * cols + c];
+    for (int64_t j = 0; j < nrg; ++j)
+        for (int64_t c = 0; c < cols; ++c) st[c * nrg + j] = s[j * cols + c];
+    free(q); free(s);
+    return 0;
+}
+
 /* MXFP8 dequantization: bf16_RNE(E4M3(q) * 2^(s-127)).  The product is exact
  * in double; NaN (code or scale 0xFF) gives the quiet NaN with the code's
  * sign.  axis 1: scale [rows, cols/32]; axis 0: scale [ceil(rows/32), cols]. */

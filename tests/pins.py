@@ -298,6 +298,19 @@ def pin_mx_colwise_is_rowwise_of_transpose(orc, x):
     assert np.array_equal(sc, st.T)
 
 
+def pin_mx_colwise_t_is_rowwise_of_transpose(orc, x):
+    """The transposed column-wise layout is row-wise MXFP8 of x transposed
+    (rows zero-padded to a multiple of 32, then cropped)."""
+    rows, cols = x.shape
+    qt, st = orc.mxfp8_quantize_colwise_t(x)
+    prow = (rows + 31) // 32 * 32
+    xp = np.zeros((prow, cols), np.uint16)
+    xp[:rows] = x
+    qr, sr = orc.mxfp8_quantize_rowwise(np.ascontiguousarray(xp.T))
+    assert np.array_equal(qt, qr[:, :rows])
+    assert np.array_equal(st, sr)
+
+
 def pin_mx_dequant_vs_torch(orc):
     """Every (code, scale byte) pair: bf16 RNE of the exact product, via torch
     (fp32 product is exact here; torch's fp32 -> bf16 cast is RNE)."""

@@ -33,6 +33,7 @@ MUTANTS = [
     ("mxfp4 dequant scale index", "uint8_t s = scale[r * (cols / MX_GROUP) + c / MX_GROUP];",
      "uint8_t s = scale[r * (cols / MX_GROUP) + (c % (cols / MX_GROUP))];"),
     ("colwise scale transposed", "scale[j * cols + c] = s;", "scale[c * nrg + j] = s;"),
+    ("colwise_t scale index", "st[c * nrg + j] = s[j * cols + c];", "st[c * nrg + j] = s[c];"),
     ("colwise group stride", "q[(r0 + i) * cols + c] = mx_encode(g[i], s);",
      "q[(r0 + i) * cols + c] = mx_encode(g[i], (uint8_t)(s + (i == 31)));"),
     ("blockfp8 divisor 447", "S = (float)amax / 448.0f;", "S = (float)amax / 447.0f;"),
@@ -78,6 +79,7 @@ def all_pins(orc):
     pins.pin_mx_max_code_band(orc, x)
     pins.pin_mx_padcrop(orc, x)
     pins.pin_mx_colwise_is_rowwise_of_transpose(orc, workloads.random_bf16((70, 96), 18))
+    pins.pin_mx_colwise_t_is_rowwise_of_transpose(orc, workloads.random_bf16((70, 96), 18))
     pins.pin_mx_dequant_vs_torch(orc)
     pins.pin_mx_roundtrip(orc, workloads.mx_small())
     pins.pin_blockfp8(orc, workloads.random_bf16((200, 300), 19), 128)

@@ -71,6 +71,11 @@ def test_mx_colwise_is_rowwise_of_transpose(orc, shape):
     pins.pin_mx_colwise_is_rowwise_of_transpose(orc, workloads.random_bf16(shape, 200 + shape[0]))
 
 
+@pytest.mark.parametrize("shape", [(64, 96), (33, 64), (1, 32), (100, 160), (31, 7)])
+def test_mx_colwise_t_is_rowwise_of_transpose(orc, shape):
+    pins.pin_mx_colwise_t_is_rowwise_of_transpose(orc, workloads.random_bf16(shape, 250 + shape[0]))
+
+
 def test_mx_dequant_all_codes_all_scales(orc):
     pins.pin_mx_dequant_vs_torch(orc)
 
