@@ -130,6 +130,8 @@ def main():
                 "qr": torch.empty((rows, cols), dtype=torch.uint8, device=dev),
                 "sr": torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
                 "fq": torch.empty((rows, cols), dtype=torch.bfloat16, device=dev),
+                "qt": torch.empty((cols, rows), dtype=torch.uint8, device=dev),
+                "st": torch.empty((cols, (rows + 31) // 32), dtype=torch.uint8, device=dev),
                 "q4": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
                 "s4": torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)}
 
@@ -260,6 +262,17 @@ def main():
         breakdown["act_16384 fake-quant only"] = rotated(
             [lambda d=d: check(lib.mxq_fake_quant(P(d["x"]), rows, cols, 1, P(d["fq"]), sp),
                                "fake_quant") for d in batches], 4 * e)
+        # column-wise in the transposed (backward-pass) layout, with and
+        # without the row-wise outputs of the same pass
+        breakdown["act_16384 one-pass, column-wise transposed"] = rotated(
+            [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]), rows,
+                                                          P(d["st"]), P(d["qr"]), P(d["sr"]),
+                                                          P(d["fq"]), sp), "colwise_t")
+             for d in batches], step_bytes)
+        breakdown["act_16384 column-wise transposed only"] = rotated(
+            [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]), rows,
+                                                          P(d["st"]), None, None, None, sp),
+                               "colwise_t") for d in batches], 2 * e + e + e // 32)
         # MXFP4 on the same batches: quantize, simulate-QAT, dequantize
         m4 = 2 * e + e // 2 + e // 32
         breakdown["act_16384 MXFP4 quantize"] = rotated(

@@ -45,6 +45,7 @@ SIGNATURES = {
     "mxq_abi_version": (ctypes.c_int, []),
     "mxq_quantize_rowwise": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "mxq_quantize_colwise": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mxq_quantize_colwise_t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "mxq_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
     "mxq_fake_quant": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
     "mxq_grouped_workspace_size": (_sz, [_i32]),
@@ -170,6 +171,37 @@ def quantize_colwise(x: torch.Tensor, rowwise: bool = True, fake_quant: bool = T
                                      _ptr(out.get("q_row")), _ptr(out.get("s_row")),
                                      _ptr(out.get("fq")), _stream(x))
     _check("mxq_quantize_colwise", st)
+    return out
+
+
+def quantize_colwise_t(x: torch.Tensor, rowwise: bool = True, fake_quant: bool = True):
+    """Column-wise MXFP8 of a 2-D bf16 tensor in the transposed layout, plus
+    optional row-wise outputs, in one pass.  Returns a dict with "q_colT"
+    uint8 [cols, rows] (a view of a [cols, ldt] buffer, ldt = rows rounded up
+    to 16), "s_colT" uint8 [cols, ceil(rows/32)] and, as requested, "q_row",
+    "s_row", "fq"."""
+    _need_bf16_cuda(x)
+    if x.dim() != 2:
+        raise ValueError("quantize_colwise_t expects a 2-D tensor")
+    x = x.contiguous()
+    rows, cols = x.shape
+    dev = x.device
+    ldt = (rows + 15) // 16 * 16
+    qt_buf = torch.empty((cols, ldt), dtype=torch.uint8, device=dev)
+    st = torch.empty((cols, (rows + MX_GROUP - 1) // MX_GROUP), dtype=torch.uint8, device=dev)
+    out = {"q_colT": qt_buf[:, :rows], "s_colT": st}
+    qr = sr = fq = None
+    if rowwise:
+        qr = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        sr = torch.empty((rows, cols // MX_GROUP if cols % MX_GROUP == 0 else 0),
+                         dtype=torch.uint8, device=dev)
+        out["q_row"], out["s_row"] = qr, sr
+    if fake_quant:
+        fq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+        out["fq"] = fq
+    st_ = load().mxq_quantize_colwise_t(_ptr(x), rows, cols, _ptr(qt_buf), ldt, _ptr(st), _ptr(qr),
+                                        _ptr(sr), _ptr(fq), _stream(x))
+    _check("mxq_quantize_colwise_t", st_)
     return out
 
 

@@ -28,6 +28,10 @@ hipError_t launch_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols, uint
                              uint8_t *sc, uint8_t *qr, uint8_t *sr, uint16_t *fq_row,
                              uint16_t *fq_col, hipStream_t stream);
 
+hipError_t launch_mx_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qt,
+                               int64_t ldt, uint8_t *st, uint8_t *qr, uint8_t *sr,
+                               uint16_t *fq_row, hipStream_t stream);
+
 hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
                              int axis, uint16_t *out, hipStream_t stream);
 

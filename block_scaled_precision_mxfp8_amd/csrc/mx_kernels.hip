@@ -128,13 +128,21 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
 // Column codes go through the hardware convert two rows at a time (the pair
 // it converts must share one scale, i.e. one column).
 // ---------------------------------------------------------------------------
-template <bool kCol, bool kRow, bool kFQRow, bool kFQCol, bool kFull>
+// kColT: column codes go to the transposed layout instead: staged in LDS as
+// lds_t[column slot][row] (column slot j*64 + lane for the lane's column j,
+// kTPitch dwords per slot) for the workgroup to write out as whole rows of
+// qt; the column scales are staged after them, one dword (the workgroup's 4
+// groups) per column, for st [cols, nrg].
+constexpr int kTPitch = 33;  // dwords per LDS column slot: 128 rows of codes + 1 (no bank conflicts)
+
+template <bool kCol, bool kColT, bool kRow, bool kFQRow, bool kFQCol, bool kFull>
 __device__ __forceinline__ void mx_colwise_body(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qc,
     uint8_t *__restrict__ sc, uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
-    uint16_t *__restrict__ fq_row, uint16_t *__restrict__ fq_col, int64_t g, int64_t col)
+    uint16_t *__restrict__ fq_row, uint16_t *__restrict__ fq_col, int64_t g, int64_t col,
+    uint32_t *__restrict__ lds_t, uint8_t *__restrict__ st, int64_t nrg)
 {
-    constexpr bool kColAny = kCol || kFQCol;
+    constexpr bool kColAny = kCol || kColT || kFQCol;
     constexpr bool kRowAny = kRow || kFQRow;
     const bool cin = kFull || col < cols;
     const int64_t r0 = g * 32;
@@ -182,6 +190,14 @@ __device__ __forceinline__ void mx_colwise_body(
             const uint32_t lo = s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24);
             const uint32_t hi = s[4] | (s[5] << 8) | (s[6] << 16) | (s[7] << 24);
             st8<kNTStore>(sc + g * cols + col, make_uint2(lo, hi));
+        }
+        if (kColT && cin) {
+            // byte `wave` of the column's dword: the workgroup's 4 groups of it
+            uint8_t *lds_s = reinterpret_cast<uint8_t *>(lds_t + kSeg * kTPitch);
+            const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+            const int ln = threadIdx.x & (kWave - 1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) lds_s[(ln * 8 + j) * 4 + wv] = (uint8_t)s[j];
         }
         col_slow = wave_any(any_nan);  // a NaN/Inf column in the wave: exact software path
     }
@@ -238,9 +254,16 @@ __device__ __forceinline__ void mx_colwise_body(
         }
     };
 
+    // kColT: codes of rows i-2, i-1 wait here until rows i, i+1 complete a 4-row
+    // dword per column
+    uint32_t tq[4] = {0u, 0u, 0u, 0u};
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
     static_for<0, 32, 2>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         if (kColAny) {
+            uint32_t a0, a1, b0, b1;  // rows i and i+1: columns 0-3 and 4-7 of the lane
             if (!col_slow) {
                 // the pair fed to one convert shares a scale: same column, rows i and i+1
                 const uint32_t a[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -250,18 +273,46 @@ __device__ __forceinline__ void mx_colwise_body(
                 for (int k = 0; k < 4; ++k)
                     rp[k] = e4m3_colpair_hw(clamp_mag2(a[k], lim2[k]), clamp_mag2(b[k], lim2[k]),
                                             sf[2 * k], sf[2 * k + 1]);
-                put_col_row(i, __builtin_amdgcn_perm(rp[1], rp[0], 0x06040200u),
-                            __builtin_amdgcn_perm(rp[3], rp[2], 0x06040200u));
-                put_col_row(i + 1, __builtin_amdgcn_perm(rp[1], rp[0], 0x07050301u),
-                            __builtin_amdgcn_perm(rp[3], rp[2], 0x07050301u));
+                a0 = __builtin_amdgcn_perm(rp[1], rp[0], 0x06040200u);
+                a1 = __builtin_amdgcn_perm(rp[3], rp[2], 0x06040200u);
+                b0 = __builtin_amdgcn_perm(rp[1], rp[0], 0x07050301u);
+                b1 = __builtin_amdgcn_perm(rp[3], rp[2], 0x07050301u);
             } else {
+                a0 = e4m3x4_col(v[i].x, v[i].y, e[0], e[1], e[2], e[3], nan[0], nan[1], nan[2],
+                                nan[3]);
+                a1 = e4m3x4_col(v[i].z, v[i].w, e[4], e[5], e[6], e[7], nan[4], nan[5], nan[6],
+                                nan[7]);
+                b0 = e4m3x4_col(v[i + 1].x, v[i + 1].y, e[0], e[1], e[2], e[3], nan[0], nan[1],
+                                nan[2], nan[3]);
+                b1 = e4m3x4_col(v[i + 1].z, v[i + 1].w, e[4], e[5], e[6], e[7], nan[4], nan[5],
+                                nan[6], nan[7]);
+            }
+            put_col_row(i, a0, a1);
+            put_col_row(i + 1, b0, b1);
+            if (kColT) {
+                if (i % 4 == 0) {
+                    tq[0] = a0; tq[1] = a1; tq[2] = b0; tq[3] = b1;
+                } else {
+                    // 4x4 byte transposes: rows i-2..i+1 x columns -> one dword
+                    // (4 consecutive rows) per column
+                    uint32_t cw[8];
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    put_col_row(i + h,
-                                e4m3x4_col(v[i + h].x, v[i + h].y, e[0], e[1], e[2], e[3], nan[0],
-                                           nan[1], nan[2], nan[3]),
-                                e4m3x4_col(v[i + h].z, v[i + h].w, e[4], e[5], e[6], e[7], nan[4],
-                                           nan[5], nan[6], nan[7]));
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t w0 = tq[h], w1 = tq[2 + h], w2 = h ? a1 : a0,
+                                       w3 = h ? b1 : b0;
+                        const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+                        const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+                        const uint32_t lo23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+                        const uint32_t hi23 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+                        cw[4 * h + 0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+                        cw[4 * h + 1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+                        cw[4 * h + 2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+                        cw[4 * h + 3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        lds_t[(j * kWave + lane) * kTPitch + wave * 8 + i / 4] = cw[j];
+                }
             }
         }
         if (kRowAny) {
@@ -286,11 +337,88 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int64_t g = rb * (kColTileRows / 32) + wave;  // 32-row group index
     if (g * 32 >= rows) return;  // wave-uniform; the kernel has no barriers
     if ((seg + 1) * kSeg <= cols && g * 32 + 32 <= rows)
-        mx_colwise_body<kCol, kRow, kFQRow, kFQCol, true>(x, rows, cols, qc, sc, qr, sr, fq_row,
-                                                          fq_col, g, col);
+        mx_colwise_body<kCol, false, kRow, kFQRow, kFQCol, true>(
+            x, rows, cols, qc, sc, qr, sr, fq_row, fq_col, g, col, nullptr, nullptr, 0);
     else
-        mx_colwise_body<kCol, kRow, kFQRow, kFQCol, false>(x, rows, cols, qc, sc, qr, sr, fq_row,
-                                                           fq_col, g, col);
+        mx_colwise_body<kCol, false, kRow, kFQRow, kFQCol, false>(
+            x, rows, cols, qc, sc, qr, sr, fq_row, fq_col, g, col, nullptr, nullptr, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Column-wise in the transposed layout (+ optional row-wise and fake-quant),
+// one read of x.  The four waves of a workgroup quantize 128 rows x 512
+// columns as above, staging the column codes and scales in LDS; after a
+// barrier the workgroup writes them out: column c's 128 codes are 128
+// contiguous bytes of qt (8 lanes, 16-byte stores) and its 4 scales one
+// dword of st.  Measured on MI355X against alternatives (cold [16384, 7168]
+// input, column codes only): codes stored straight from registers, 16-byte
+// pieces of 64 lines per instruction, 3.1 TB/s (1.4 with streaming stores);
+// scale bytes stored straight from registers 4.67 TB/s; this form 4.87; a
+// persistent workgroup prefetching its next tile spills registers, 4.0.
+// ---------------------------------------------------------------------------
+template <bool kRow, bool kFQRow>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mx_colwise_t_kernel(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qt,
+    int64_t ldt, uint8_t *__restrict__ st, uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
+    uint16_t *__restrict__ fq_row, int64_t nseg)
+{
+    __shared__ uint32_t lds_t[kSeg * kTPitch + kSeg];
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSeg + lane * 8;
+    const int64_t g = rb * (kColTileRows / 32) + wave;  // 32-row group index
+    const int64_t nrg = (rows + 31) / 32;
+    if (g * 32 < rows) {  // wave-uniform; every wave reaches the barrier below
+        if ((seg + 1) * kSeg <= cols && g * 32 + 32 <= rows)
+            mx_colwise_body<false, true, kRow, kFQRow, false, true>(
+                x, rows, cols, nullptr, nullptr, qr, sr, fq_row, nullptr, g, col, lds_t, st, nrg);
+        else
+            mx_colwise_body<false, true, kRow, kFQRow, false, false>(
+                x, rows, cols, nullptr, nullptr, qr, sr, fq_row, nullptr, g, col, lds_t, st, nrg);
+    }
+    __syncthreads();
+    {
+        // scales: the tile's 4 groups of each column, one dword when st rows
+        // are dword-aligned (nrg % 4 == 0; st itself is 4-byte aligned)
+        const uint32_t *lds_s = lds_t + kSeg * kTPitch;
+        const int64_t g0 = rb * 4;
+        for (int cl = threadIdx.x; cl < kSeg; cl += 256) {
+            const int64_t c = seg * kSeg + cl;
+            if (c >= cols) continue;
+            const uint32_t w4 = lds_s[cl];
+            if (g0 + 4 <= nrg && (nrg & 3) == 0) {
+                *reinterpret_cast<uint32_t *>(st + c * nrg + g0) = w4;
+            } else {
+                for (int b = 0; b < 4 && g0 + b < nrg; ++b)
+                    st[c * nrg + g0 + b] = (uint8_t)(w4 >> (8 * b));
+            }
+        }
+    }
+    // write-out: LDS slot ridx holds column (ridx % 64) * 8 + ridx / 64 of the
+    // segment; 8 threads per slot, 16 rows (one dword quad) each.  Rows and
+    // columns past the tensor's edge hold codes of nothing and are skipped.
+    const int k = threadIdx.x & 7;
+    const int64_t r = rb * kColTileRows + k * 16;
+#pragma unroll 4
+    for (int it = 0; it < kSeg / 32; ++it) {
+        const int ridx = it * 32 + (threadIdx.x >> 3);
+        const int64_t c = seg * kSeg + (ridx & (kWave - 1)) * 8 + (ridx >> 6);
+        const uint32_t *src = lds_t + ridx * kTPitch + k * 4;
+        const uint4 w = make_uint4(src[0], src[1], src[2], src[3]);
+        if (c >= cols || r >= rows) continue;
+        uint8_t *dst = qt + c * ldt + r;
+        if (r + 16 <= rows) {
+            st16<kNTStore>(dst, w);
+        } else {
+            for (int b = 0; b < (int)(rows - r); ++b) {
+                const uint32_t word = b < 4 ? w.x : b < 8 ? w.y : b < 12 ? w.z : w.w;
+                dst[b] = (uint8_t)(word >> (8 * (b & 3)));
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -440,6 +568,26 @@ hipError_t launch_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols, uint
     else if (fq_col) MXQ_COLWISE(false, false, false, true);
     else return hipErrorInvalidValue;
 #undef MXQ_COLWISE
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qt,
+                               int64_t ldt, uint8_t *st, uint8_t *qr, uint8_t *sr,
+                               uint16_t *fq_row, hipStream_t stream)
+{
+    const int64_t nseg = (cols + kSeg - 1) / kSeg;
+    const int64_t tiles = nseg * ((rows + kColTileRows - 1) / kColTileRows);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)tiles), block(256);
+#define MXQ_COLWISE_T(R, FR)                                                                       \
+    hipLaunchKernelGGL((mx_colwise_t_kernel<R, FR>), grid, block, 0, stream, x, rows, cols, qt,    \
+                       ldt, st, qr, sr, fq_row, nseg)
+    if (qr && fq_row) MXQ_COLWISE_T(true, true);
+    else if (qr) MXQ_COLWISE_T(true, false);
+    else if (fq_row) MXQ_COLWISE_T(false, true);
+    else MXQ_COLWISE_T(false, false);
+#undef MXQ_COLWISE_T
     return hipGetLastError();
 }
 

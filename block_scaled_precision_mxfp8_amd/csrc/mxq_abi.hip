@@ -132,6 +132,23 @@ mxq_status mxq_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, int axi
     return from_hip(e);
 }
 
+mxq_status mxq_quantize_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qt,
+                                  int64_t ldt, uint8_t *st, uint8_t *qr, uint8_t *sr,
+                                  uint16_t *fq, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !qt || !st || (qr && !sr) || (sr && !qr)) return MXQ_EINVAL;
+    if (ldt < rows) return MXQ_ESHAPE;
+    if (!aligned(x, 16) || !aligned(qt, 16) || ldt % 16 != 0 || !aligned(st, 4)) return MXQ_EALIGN;
+    if (qr && !aligned(qr, 8)) return MXQ_EALIGN;
+    if (fq && !aligned(fq, 16)) return MXQ_EALIGN;
+    if (!fits(rows, cols) || !fits(cols, ldt)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_mx_colwise_t(x, rows, cols, qt, ldt, st, qr, sr, fq,
+                                             as_stream(stream)));
+}
+
 mxq_status mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
                           uint8_t *scale, uint16_t *fq, void *stream)
 {

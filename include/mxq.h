@@ -105,6 +105,26 @@ mxq_status mxq_quantize_colwise(const uint16_t *x, int64_t rows, int64_t cols,
                                 uint8_t *qr, uint8_t *sr, uint16_t *fq, void *stream);
 
 /*
+ * Column-wise MXFP8 in the transposed layout a backward-pass (weight-gradient)
+ * GEMM reads, with optional row-wise outputs, in one read of x.  The groups,
+ * scales and codes are those of mxq_quantize_colwise (32 consecutive rows of
+ * one column; a short last group equals zero padding); only the storage
+ * differs, which makes qt / st the row-wise MXFP8 of x transposed:
+ *   qt  [cols, rows] E4M3 codes, row stride ldt bytes: qt[c * ldt + r] is the
+ *       code of x[r, c]; ldt >= rows, ldt % 16 == 0, qt 16-byte aligned
+ *   st  [cols, ceil(rows/32)] E8M0 bytes, compact, 4-byte aligned:
+ *       st[c * ceil(rows/32) + j] is the scale of rows 32j..32j+31 of column c
+ *   qr, sr, fq  optional row-wise codes [rows, cols], scales [rows, cols/32]
+ *       and row-wise fake-quant [rows, cols] bf16, as mxq_quantize_colwise
+ *       (qr and sr together or neither; fq alone is allowed)
+ * x [rows, cols] bf16 contiguous, 16-byte aligned.  Shape: cols % 32 == 0;
+ * any rows >= 0.  Bytes of qt between rows and ldt are not written.
+ */
+mxq_status mxq_quantize_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qt,
+                                  int64_t ldt, uint8_t *st, uint8_t *qr, uint8_t *sr,
+                                  uint16_t *fq, void *stream);
+
+/*
  * MXFP8 dequantization: out = bf16_RNE(E4M3(q) * 2^(scale - 127)).  NaN code
  * or scale byte 0xFF gives the quiet NaN 0x7FC0 with the code's sign bit.
  *   q      [rows, cols] E4M3, contiguous

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
                  "mxq_quantize_rowwise_grouped", "blockfp8_quantize", "blockfp8_dequantize",
                  "nvfp4_quantize", "nvfp4_dequantize", "mxq_status_string", "mxq_abi_version",
                  "mxq_grouped_workspace_size", "nvfp4_workspace_size", "mxfp4_quantize",
-                 "mxfp4_dequantize", "mxfp4_fake_quant"]:
+                 "mxfp4_dequantize", "mxfp4_fake_quant", "mxq_quantize_colwise_t"]:
         assert want in names
     assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
 
@@ -149,6 +149,24 @@ def test_blockfp8_nvfp4_errors(lib):
     assert nd(P16, P16, NULL, 4, 32, P16, NULL) == mxq.MXQ_EINVAL
     assert nd(P16, P16, P16, 4, 32, P8, NULL) == mxq.MXQ_EALIGN
     assert nd(NULL, NULL, NULL, 0, 32, NULL, NULL) == mxq.MXQ_OK
+
+
+def test_colwise_t_errors(lib):
+    f = lib.mxq_quantize_colwise_t
+    assert f(P16, -1, 32, P16, 16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 48, P16, 16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_ESHAPE   # cols % 32
+    assert f(NULL, 4, 32, P16, 16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, NULL, 16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, P16, 16, NULL, NULL, NULL, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, P16, 16, P16, P16, NULL, NULL, NULL) == mxq.MXQ_EINVAL    # qr without sr
+    assert f(P16, 40, 32, P16, 32, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_ESHAPE  # ldt < rows
+    assert f(P16, 4, 32, P16, 24, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EALIGN   # ldt % 16
+    assert f(P16, 4, 32, P8, 16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EALIGN    # qt 16-aligned
+    assert f(P8, 4, 32, P16, 16, P16, NULL, NULL, NULL, NULL) == mxq.MXQ_EALIGN
+    assert f(P16, 4, 32, P16, 16, P16, P4, P16, NULL, NULL) == mxq.MXQ_EALIGN      # qr 8-aligned
+    assert f(P16, 4, 32, P16, 16, P16, NULL, NULL, P8, NULL) == mxq.MXQ_EALIGN     # fq 16-aligned
+    assert f(P16, 4, 32, P16, 16, P2, NULL, NULL, NULL, NULL) == mxq.MXQ_EALIGN    # st 4-aligned
+    assert f(NULL, 0, 32, NULL, 0, NULL, NULL, NULL, NULL, NULL) == mxq.MXQ_OK
 
 
 def test_mxfp4_errors(lib):
