@@ -98,6 +98,8 @@ class Oracle:
         L.orc_blockfp8_quantize.restype = None
         L.orc_blockfp8_dequantize.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int32, _u16p]
         L.orc_blockfp8_dequantize.restype = None
+        L.orc_blockfp8_to_mxfp8.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int32, _u8p, _u8p]
+        L.orc_blockfp8_to_mxfp8.restype = ctypes.c_int
         L.orc_nvfp4_quantize.argtypes = [_u16p, _i64, _i64, _u8p, _u8p, _f32p]
         L.orc_nvfp4_quantize.restype = None
         L.orc_nvfp4_dequantize.argtypes = [_u8p, _u8p, _f32p, _i64, _i64, _u16p]
@@ -236,6 +238,20 @@ class Oracle:
         self.L.orc_blockfp8_dequantize(_p(q, _u8p), _p(S, _f32p), rows, cols, int(blk),
                                        _p(out, _u16p))
         return out
+
+    def blockfp8_to_mxfp8(self, q: np.ndarray, S: np.ndarray, blk: int = 128):
+        """Block-FP8 (codes + fp32 tile scales) -> bf16 -> row-wise MXFP8:
+        (q8 [rows, cols] u8, scale [rows, cols/32] u8)."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        S = np.ascontiguousarray(S, dtype=np.float32)
+        rows, cols = q.shape
+        assert cols % 32 == 0
+        q8 = np.empty((rows, cols), np.uint8)
+        s8 = np.empty((rows, cols // 32), np.uint8)
+        rc = self.L.orc_blockfp8_to_mxfp8(_p(q, _u8p), _p(S, _f32p), rows, cols, int(blk),
+                                          _p(q8, _u8p), _p(s8, _u8p))
+        assert rc == 0
+        return q8, s8
 
     # ---- NVFP4 ------------------------------------------------------------
     def nvfp4_quantize(self, x: np.ndarray):

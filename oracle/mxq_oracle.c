@@ -490,6 +490,22 @@ void orc_blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows,
         }
 }
 
+/* FP8 block -> BF16 -> MXFP8 re-quantization [MX-adapter, 实现拆解 item 5:
+ * the FP8->BF16->MXFP8 checkpoint conversion]: dequantize a block-FP8 tensor
+ * (codes q [rows, cols], fp32 scales [ceil(rows/blk), ceil(cols/blk)]) to
+ * bf16 as orc_blockfp8_dequantize does, then quantize that bf16 tensor
+ * row-wise to MXFP8.  cols % 32 == 0. */
+int orc_blockfp8_to_mxfp8(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                          int32_t blk, uint8_t *q8, uint8_t *scale8)
+{
+    uint16_t *bf = (uint16_t *)malloc((size_t)(rows * cols) * sizeof(uint16_t));
+    if (!bf) return -1;
+    orc_blockfp8_dequantize(q, scale, rows, cols, blk, bf);
+    orc_mxfp8_quantize_rowwise(bf, rows, cols, q8, scale8);
+    free(bf);
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* NVFP4: global fp32 scale, per-16 E4M3 block scale, E2M1 elements          */
 /* [xorl, "What looked solid"; V4-mxfp4, review of fp4_act_quant]            */

@@ -587,3 +587,42 @@ def pin_mx4_roundtrip(orc, x):
     err = np.abs(dv - xv)
     assert np.all(err[fin & ~sat] <= half_ulp[fin & ~sat])
     assert np.array_equal(err[fin & sat], (np.abs(xv) - 6 * X)[fin & sat])
+
+
+# ---------------------------------------------------------------------------
+# FP8 block -> BF16 -> MXFP8 re-quantization pins
+# ---------------------------------------------------------------------------
+
+def pin_requant_pow2_tiles(orc, rows=256, cols=384, seed=8):
+    """Closed form: with a power-of-two tile scale S = 2^k, the bf16
+    intermediate is exactly E4M3(q) * 2^k, and every MX group whose largest
+    code magnitude lies in [256, 448] (codes 0x78..0x7E) gets scale byte
+    k + 127 and its input codes back unchanged."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 256, size=(rows, cols)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x7E                      # no NaN codes
+    tr, tc = -(-rows // 128), -(-cols // 128)
+    k = rng.integers(-20, 20, size=(tr, tc))
+    S = np.exp2(k.astype(np.float64)).astype(np.float32)
+    q8, s8 = orc.blockfp8_to_mxfp8(q, S)
+    gmax = (q.reshape(rows, cols // 32, 32) & 0x7F).max(axis=-1)
+    kk = np.repeat(np.repeat(k, 128, 0), 128, 1)[:rows, :cols][:, ::32]
+    big = (gmax >= 0x78) & (gmax <= 0x7E)
+    assert big.any()
+    assert np.array_equal(s8[big].astype(np.int64), kk[big] + 127)
+    bm = np.repeat(big, 32, axis=1)
+    assert np.array_equal(q8[bm], q[bm])
+
+
+def pin_requant_matches_steps(orc, x):
+    """Against torch: the block-FP8 dequantization as torch fp32 products and
+    its bf16 cast, then the row-wise MXFP8 of that bf16 tensor through the
+    (separately pinned) row-wise oracle."""
+    q, S = orc.blockfp8_quantize(x, 128)
+    rows, cols = q.shape
+    Sx = np.repeat(np.repeat(S, 128, 0), 128, 1)[:rows, :cols]
+    v = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).float() * torch.from_numpy(Sx)
+    bf = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q8, s8 = orc.blockfp8_to_mxfp8(q, S)
+    rq, rs = orc.mxfp8_quantize_rowwise(bf)
+    assert np.array_equal(q8, rq) and np.array_equal(s8, rs)

@@ -181,3 +181,13 @@ def test_mx4_roundtrip_and_idempotence(orc, which):
     else:
         x = workloads.weight_4097()[:256]
     pins.pin_mx4_roundtrip(orc, np.ascontiguousarray(x))
+
+
+def test_requant_pow2_tiles_keep_codes(orc):
+    pins.pin_requant_pow2_tiles(orc)
+
+
+@pytest.mark.parametrize("which", ["normal", "outliers"])
+def test_requant_matches_steps(orc, which):
+    x = workloads.random_bf16((200, 384), 17) if which == "normal" else workloads.square_8192(n=256)
+    pins.pin_requant_matches_steps(orc, x)
