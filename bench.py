@@ -353,6 +353,8 @@ def main():
                 "bq": torch.empty((n_, n_), dtype=torch.uint8, device=dev),
                 "bS": torch.empty((n_ // 128, n_ // 128), dtype=torch.float32, device=dev),
                 "bd": torch.empty((n_, n_), dtype=torch.bfloat16, device=dev),
+                "rq8": torch.empty((n_, n_), dtype=torch.uint8, device=dev),
+                "rs8": torch.empty((n_, n_ // 32), dtype=torch.uint8, device=dev),
                 "nq": torch.empty((n_, n_ // 2), dtype=torch.uint8, device=dev),
                 "ns": torch.empty((n_, n_ // 16), dtype=torch.uint8, device=dev),
                 "ng": torch.empty((1,), dtype=torch.float32, device=dev),
@@ -365,6 +367,10 @@ def main():
             [lambda d=d: check(lib.blockfp8_dequantize(P(d["bq"]), P(d["bS"]), n_, n_, 128,
                                                        P(d["bd"]), sp), "bfp8 dq") for d in ysets],
             bbytes)
+        breakdown["square_8192 block-FP8 -> MXFP8 re-quantize (one pass)"] = rotated(
+            [lambda d=d: check(lib.blockfp8_to_mxfp8(P(d["bq"]), P(d["bS"]), n_, n_, 128,
+                                                     P(d["rq8"]), P(d["rs8"]), sp), "requant")
+             for d in ysets], ye + 4 * (n_ // 128) ** 2 + ye + ye // 32)
         breakdown["square_8192 NVFP4 quantize (unique bytes)"] = rotated(
             [lambda d=d: check(lib.nvfp4_quantize(P(d["y"]), n_, n_, P(d["nq"]), P(d["ns"]),
                                                   P(d["ng"]), P(d["nws"]), nwsz, sp), "nvfp4")

@@ -52,6 +52,7 @@ SIGNATURES = {
     "mxq_quantize_rowwise_grouped": (ctypes.c_int, [_vp, _i32, _vp, _sz, _vp]),
     "blockfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "blockfp8_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "blockfp8_to_mxfp8": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "mxfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "mxfp4_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "mxfp4_fake_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
@@ -331,6 +332,24 @@ def mxfp4_simulate_qat(x: torch.Tensor) -> torch.Tensor:
     st = load().mxfp4_fake_quant(_ptr(x2), rows, cols, _ptr(out), _stream(x2))
     _check("mxfp4_fake_quant", st)
     return out.view(x.shape)
+
+
+def blockfp8_to_mxfp8(q: torch.Tensor, S: torch.Tensor, blk: int = 128):
+    """Block-FP8 (E4M3 codes [rows, cols] + fp32 tile scales) re-quantized
+    through bf16 to row-wise MXFP8 in one pass: (q8 uint8 [rows, cols],
+    scale uint8 [rows, cols/32])."""
+    if not q.is_cuda:
+        raise ValueError("q must live on the GPU (the library has no CPU path)")
+    q = q.contiguous()
+    S = S.contiguous()
+    rows, cols = q.shape
+    q8 = torch.empty((rows, cols), dtype=torch.uint8, device=q.device)
+    s8 = torch.empty((rows, cols // MX_GROUP if cols % MX_GROUP == 0 else 0), dtype=torch.uint8,
+                     device=q.device)
+    st = load().blockfp8_to_mxfp8(_ptr(q.view(torch.uint8)), _ptr(S), rows, cols, blk, _ptr(q8),
+                                  _ptr(s8), _stream(q))
+    _check("blockfp8_to_mxfp8", st)
+    return q8, s8
 
 
 def nvfp4_workspace(device) -> torch.Tensor:

@@ -179,6 +179,53 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
 }
 
 // ---------------------------------------------------------------------------
+// FP8 block -> BF16 -> MXFP8 in one pass (the checkpoint conversion): each
+// lane dequantizes 8 codes of a row exactly as bfp8_dequant_kernel does and
+// quantizes the 8 bf16 row-wise as the MXFP8 row-wise kernel does (a lane
+// quad is one group of 32), so the bf16 tensor never reaches memory: 1 byte
+// read and 1 + 1/32 written per element instead of 6.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bfp8_to_mx_kernel(const uint8_t *__restrict__ q,
+                                                         const float *__restrict__ scale,
+                                                         int64_t rows, int64_t cols,
+                                                         uint8_t *__restrict__ q8,
+                                                         uint8_t *__restrict__ s8, int64_t tc,
+                                                         int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSegNv + lane * 8;
+    if (col >= cols) return;  // cols % 32 == 0: whole quads leave; no barriers below
+    const int64_t r0 = rb * kRowsNv + wave;
+    const float S = scale[((rb * kRowsNv) / kBlk) * tc + col / kBlk];
+    constexpr int kR = kRowsNv / 4;
+    uint2 c[kR];
+    bool nan_code = false;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        c[i] = make_uint2(0, 0);
+        if (r < rows) c[i] = ld8<kNTLoadDq>(q + r * cols + col);
+        const uint32_t tx = c[i].x & 0x7F7F7F7Fu, ty = c[i].y & 0x7F7F7F7Fu;
+        nan_code |= (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
+    }
+    const bool slow = wave_any(nan_code || !__builtin_isfinite(S));
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        const uint4 bf = slow ? bfp8_dequant8(c[i], S, true) : bfp8_dequant8(c[i], S, false);
+        const MxRow8 m = mx_row_encode8(bf);
+        if (r < rows) {
+            st8<kNTStore>(q8 + r * cols + col, make_uint2(m.c0, m.c1));
+            s8[r * (cols >> 5) + (col >> 5)] = (uint8_t)m.s;  // same byte from a quad's 4 lanes
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // NVFP4.  Pass 1: each workgroup writes the max magnitude (bf16 bits) of its
 // share of x to a partials array; pass 2 reduces the partials (an unsigned
 // max: order-independent, deterministic) and quantizes.  In pass 2 a lane
@@ -415,6 +462,19 @@ hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t row
     const int64_t tc = (cols + kBlk - 1) / kBlk;
     hipLaunchKernelGGL(bfp8_dequant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scale,
                        rows, cols, out, tc, nseg);
+    return hipGetLastError();
+}
+
+hipError_t launch_bfp8_to_mx(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                             uint8_t *q8, uint8_t *s8, hipStream_t stream)
+{
+    const int64_t tc = (cols + kBlk - 1) / kBlk;
+    const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
+    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bfp8_to_mx_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scale,
+                       rows, cols, q8, s8, tc, nseg);
     return hipGetLastError();
 }
 

@@ -50,6 +50,9 @@ hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint
 hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
                                uint16_t *out, hipStream_t stream);
 
+hipError_t launch_bfp8_to_mx(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                             uint8_t *q8, uint8_t *s8, hipStream_t stream);
+
 // NVFP4 amax partials: at most this many workgroups write one word each.
 constexpr int kNvAmaxBlocks = 1024;
 

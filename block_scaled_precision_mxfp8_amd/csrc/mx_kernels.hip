@@ -64,17 +64,10 @@ __device__ __forceinline__ void mx_row_tile_impl(const uint16_t *__restrict__ x,
         for (int u = 0; u < kU; ++u) {
             const int64_t r = r0 + 4 * (it * kU + u);
             const bool ok = kFull || (cin && r < rows);
-            const uint32_t s = mx_scale_byte(quad_max(amax8(v[u])));
+            const MxRow8 m = mx_row_encode8(v[u]);
+            const uint32_t s = m.s, c0 = m.c0, c1 = m.c1;
+            const float sf = m.sf;
             const bool nan_group = s == 0xFFu;
-            const uint32_t lim = mx_limit_bf16(s);
-            const uint32_t lim2 = lim | (lim << 16);
-            const float sf = e8m0_to_f32(s);
-            uint32_t c0 = e4m3x4_row_hw(v[u].x, v[u].y, lim2, sf);
-            uint32_t c1 = e4m3x4_row_hw(v[u].z, v[u].w, lim2, sf);
-            if (nan_group) {
-                c0 = 0x7F7F7F7Fu | signs4(v[u].x, v[u].y);
-                c1 = 0x7F7F7F7Fu | signs4(v[u].z, v[u].w);
-            }
             if (kQ && ok) {
                 st8<kNTStore>(q + r * ldq + col, make_uint2(c0, c1));
                 // all 4 lanes of the quad hold the same byte: storing it from

@@ -268,6 +268,18 @@ mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t row
     return from_hip(mxq::launch_bfp8_dequant(q, scale, rows, cols, out, as_stream(stream)));
 }
 
+mxq_status blockfp8_to_mxfp8(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                             int32_t blk, uint8_t *q8, uint8_t *scale8, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (blk != 128 || cols % 32 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!q || !scale || !q8 || !scale8) return MXQ_EINVAL;
+    if (!aligned(q, 8) || !aligned(scale, 4) || !aligned(q8, 8)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_to_mx(q, scale, rows, cols, q8, scale8, as_stream(stream)));
+}
+
 mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
                           uint8_t *s_e4m3, float *global_scale, void *workspace,
                           size_t workspace_bytes, void *stream)

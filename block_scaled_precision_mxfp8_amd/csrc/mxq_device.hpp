@@ -295,6 +295,32 @@ __device__ __forceinline__ uint32_t e4m3x4_row_hw(uint32_t w0, uint32_t w1, uint
                            clamp_mag2(w1, lim2), scale);
 }
 
+// Row-wise MXFP8 of one lane's 8 bf16 when its lane quad holds one group of
+// 32: the group's scale byte (the same in all 4 lanes), its fp32 value, and
+// the lane's 8 E4M3 codes (elements 0..3 in c0).  A NaN/Inf group gives
+// 0x7F with each element's sign.
+struct MxRow8 {
+    uint32_t s;
+    float sf;
+    uint32_t c0, c1;
+};
+
+__device__ __forceinline__ MxRow8 mx_row_encode8(uint4 v)
+{
+    MxRow8 m;
+    m.s = mx_scale_byte(quad_max(amax8(v)));
+    const uint32_t lim = mx_limit_bf16(m.s);
+    const uint32_t lim2 = lim | (lim << 16);
+    m.sf = e8m0_to_f32(m.s);
+    m.c0 = e4m3x4_row_hw(v.x, v.y, lim2, m.sf);
+    m.c1 = e4m3x4_row_hw(v.z, v.w, lim2, m.sf);
+    if (m.s == 0xFFu) {
+        m.c0 = 0x7F7F7F7Fu | signs4(v.x, v.y);
+        m.c1 = 0x7F7F7F7Fu | signs4(v.z, v.w);
+    }
+    return m;
+}
+
 // Column groups: the pair fed to one convert must share a scale, so it is
 // made of the same column in two consecutive rows.  For dword k (columns 2k,
 // 2k+1) of rows i and i+1 (already clamped): returns bytes

@@ -191,6 +191,21 @@ mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t row
                                int32_t blk, uint16_t *out, void *stream);
 
 /*
+ * FP8 block -> BF16 -> MXFP8 re-quantization in one pass: the conversion of
+ * a block-FP8 checkpoint to MXFP8 ("PR #1935 完整报告", 实现拆解 item 5,
+ * the FP8->BF16->MXFP8 conversion).  The result equals
+ * mxq_quantize_rowwise(blockfp8_dequantize(q, scale)) byte for byte; the
+ * bf16 intermediate is never written.
+ *   q       [rows, cols] E4M3 codes, contiguous, 8-byte aligned
+ *   scale   [ceil(rows/128), ceil(cols/128)] fp32 tile scales, 4-byte aligned
+ *   q8      [rows, cols] E4M3 codes out, contiguous, 8-byte aligned
+ *   scale8  [rows, cols/32] E8M0 bytes out, contiguous
+ * Shape: blk == 128; cols % 32 == 0; any rows >= 0.
+ */
+mxq_status blockfp8_to_mxfp8(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                             int32_t blk, uint8_t *q8, uint8_t *scale8, void *stream);
+
+/*
  * MXFP4 quantization (miles PR #1372 "V4 mxfp4": mxfp4_simulate_qat with
  * groups of 32 in the compressor review; the packed [..., N/2] FP4 output in
  * the review of fp4_act_quant).  Every 32 consecutive values of a row share

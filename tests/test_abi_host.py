@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                  "mxq_quantize_rowwise_grouped", "blockfp8_quantize", "blockfp8_dequantize",
                  "nvfp4_quantize", "nvfp4_dequantize", "mxq_status_string", "mxq_abi_version",
                  "mxq_grouped_workspace_size", "nvfp4_workspace_size", "mxfp4_quantize",
-                 "mxfp4_dequantize", "mxfp4_fake_quant", "mxq_quantize_colwise_t"]:
+                 "mxfp4_dequantize", "mxfp4_fake_quant", "mxq_quantize_colwise_t",
+                 "blockfp8_to_mxfp8"]:
         assert want in names
     assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
 
@@ -167,6 +168,21 @@ def test_colwise_t_errors(lib):
     assert f(P16, 4, 32, P16, 16, P16, NULL, NULL, P8, NULL) == mxq.MXQ_EALIGN     # fq 16-aligned
     assert f(P16, 4, 32, P16, 16, P2, NULL, NULL, NULL, NULL) == mxq.MXQ_EALIGN    # st 4-aligned
     assert f(NULL, 0, 32, NULL, 0, NULL, NULL, NULL, NULL, NULL) == mxq.MXQ_OK
+
+
+def test_blockfp8_to_mxfp8_errors(lib):
+    f = lib.blockfp8_to_mxfp8
+    assert f(P16, P16, -1, 32, 128, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, P16, 4, 32, 64, P16, P16, NULL) == mxq.MXQ_ESHAPE     # blk != 128
+    assert f(P16, P16, 4, 48, 128, P16, P16, NULL) == mxq.MXQ_ESHAPE    # cols % 32
+    assert f(NULL, P16, 4, 32, 128, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, NULL, 4, 32, 128, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, P16, 4, 32, 128, NULL, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, P16, 4, 32, 128, P16, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P4, P16, 4, 32, 128, P16, P16, NULL) == mxq.MXQ_EALIGN     # q 8-aligned
+    assert f(P16, P2, 4, 32, 128, P16, P16, NULL) == mxq.MXQ_EALIGN     # scale 4-aligned
+    assert f(P16, P16, 4, 32, 128, P4, P16, NULL) == mxq.MXQ_EALIGN     # q8 8-aligned
+    assert f(NULL, NULL, 0, 32, 128, NULL, NULL, NULL) == mxq.MXQ_OK
 
 
 def test_mxfp4_errors(lib):
