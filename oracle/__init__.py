@@ -94,6 +94,14 @@ class Oracle:
         L.orc_mxfp4_dequantize.restype = None
         L.orc_mxfp4_fake_quant.argtypes = [_u16p, _i64, _i64, _u16p]
         L.orc_mxfp4_fake_quant.restype = ctypes.c_int
+        L.orc_blockfp8_quantize_rect.argtypes = [_u16p, _i64, _i64, ctypes.c_int32,
+                                                 ctypes.c_int32, _u8p, _f32p]
+        L.orc_blockfp8_quantize_rect.restype = None
+        L.orc_blockfp8_dequantize_rect.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int32,
+                                                   ctypes.c_int32, _u16p]
+        L.orc_blockfp8_dequantize_rect.restype = None
+        L.orc_blockfp8_fake_quant_1x128.argtypes = [_u16p, _i64, _i64, _u16p]
+        L.orc_blockfp8_fake_quant_1x128.restype = ctypes.c_int
         L.orc_blockfp8_quantize.argtypes = [_u16p, _i64, _i64, ctypes.c_int32, _u8p, _f32p]
         L.orc_blockfp8_quantize.restype = None
         L.orc_blockfp8_dequantize.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int32, _u16p]
@@ -237,6 +245,33 @@ class Oracle:
         out = np.empty((rows, cols), np.uint16)
         self.L.orc_blockfp8_dequantize(_p(q, _u8p), _p(S, _f32p), rows, cols, int(blk),
                                        _p(out, _u16p))
+        return out
+
+    def blockfp8_quantize_rect(self, x: np.ndarray, br: int, bc: int):
+        """br x bc blocks: (q [rows, cols] u8, S [ceil(rows/br), ceil(cols/bc)] f32)."""
+        x = _bits16(x)
+        rows, cols = x.shape
+        q = np.empty((rows, cols), np.uint8)
+        S = np.empty(((rows + br - 1) // br, (cols + bc - 1) // bc), np.float32)
+        self.L.orc_blockfp8_quantize_rect(_p(x, _u16p), rows, cols, int(br), int(bc),
+                                          _p(q, _u8p), _p(S, _f32p))
+        return q, S
+
+    def blockfp8_dequantize_rect(self, q: np.ndarray, S: np.ndarray, br: int, bc: int):
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        S = np.ascontiguousarray(S, dtype=np.float32)
+        rows, cols = q.shape
+        out = np.empty((rows, cols), np.uint16)
+        self.L.orc_blockfp8_dequantize_rect(_p(q, _u8p), _p(S, _f32p), rows, cols, int(br),
+                                            int(bc), _p(out, _u16p))
+        return out
+
+    def blockfp8_fake_quant_1x128(self, x: np.ndarray) -> np.ndarray:
+        x = _bits16(x)
+        rows, cols = x.shape
+        out = np.empty((rows, cols), np.uint16)
+        rc = self.L.orc_blockfp8_fake_quant_1x128(_p(x, _u16p), rows, cols, _p(out, _u16p))
+        assert rc == 0
         return out
 
     def blockfp8_to_mxfp8(self, q: np.ndarray, S: np.ndarray, blk: int = 128):

@@ -430,15 +430,15 @@ int orc_mxfp4_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, uint16_t
  * region.  A zero tile stores S = 0 and divides by 1 (all codes +-0).  A tile
  * holding NaN or Inf stores S = NaN and every code is NaN with x's sign.
  * scale is [ceil(rows/blk), ceil(cols/blk)] fp32 row-major. */
-void orc_blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int32_t blk,
-                           uint8_t *q, float *scale)
+void orc_blockfp8_quantize_rect(const uint16_t *x, int64_t rows, int64_t cols, int32_t br,
+                                int32_t bc, uint8_t *q, float *scale)
 {
-    int64_t tr = (rows + blk - 1) / blk, tc = (cols + blk - 1) / blk;
+    int64_t tr = (rows + br - 1) / br, tc = (cols + bc - 1) / bc;
     for (int64_t bi = 0; bi < tr; ++bi) {
         for (int64_t bj = 0; bj < tc; ++bj) {
-            int64_t r0 = bi * blk, c0 = bj * blk;
-            int64_t r1 = r0 + blk < rows ? r0 + blk : rows;
-            int64_t c1 = c0 + blk < cols ? c0 + blk : cols;
+            int64_t r0 = bi * br, c0 = bj * bc;
+            int64_t r1 = r0 + br < rows ? r0 + br : rows;
+            int64_t c1 = c0 + bc < cols ? c0 + bc : cols;
             double amax = 0.0;
             int nonfinite = 0;
             for (int64_t r = r0; r < r1; ++r)
@@ -473,21 +473,50 @@ void orc_blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int32_
     }
 }
 
+/* Square blk x blk tiles (the weight recipe). */
+void orc_blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int32_t blk,
+                           uint8_t *q, float *scale)
+{
+    orc_blockfp8_quantize_rect(x, rows, cols, blk, blk, q, scale);
+}
+
 /* Block-FP8 dequantization: bf16_RNE(fl32(E4M3(q) * S)).  A NaN product
  * (NaN code, NaN scale, 0 * Inf) gives the quiet NaN with the code's sign. */
-void orc_blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows,
-                             int64_t cols, int32_t blk, uint16_t *out)
+void orc_blockfp8_dequantize_rect(const uint8_t *q, const float *scale, int64_t rows,
+                                  int64_t cols, int32_t br, int32_t bc, uint16_t *out)
 {
-    int64_t tc = (cols + blk - 1) / blk;
+    int64_t tc = (cols + bc - 1) / bc;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c) {
             uint8_t code = q[r * cols + c];
-            float S = scale[(r / blk) * tc + c / blk];
+            float S = scale[(r / br) * tc + c / bc];
             float v = (float)orc_e4m3_to_double(code);
             float p = v * S;                    /* one IEEE fp32 multiplication */
             out[r * cols + c] = isnan(p) ? (uint16_t)((code & 0x80) ? 0xFFC0 : 0x7FC0)
                                          : orc_double_to_bf16((double)p);
         }
+}
+
+void orc_blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
+                             int32_t blk, uint16_t *out)
+{
+    orc_blockfp8_dequantize_rect(q, scale, rows, cols, blk, blk, out);
+}
+
+/* 1 x 128 blocks along each row: the activation recipe, and with
+ * dequantization right after it the fake quantization fp8_simulate_qat(x,
+ * 128) ["V4 mxfp4" (miles PR #1372), compressor review; fp32 scale storage per
+ * the PR description].  scale is [rows, ceil(cols/128)]. */
+int orc_blockfp8_fake_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint16_t *out)
+{
+    int64_t tc = (cols + 127) / 128;
+    uint8_t *q = (uint8_t *)malloc((size_t)(rows * cols));
+    float *S = (float *)malloc((size_t)(rows * tc) * sizeof(float));
+    if (!q || !S) { free(q); free(S); return -1; }
+    orc_blockfp8_quantize_rect(x, rows, cols, 1, 128, q, S);
+    orc_blockfp8_dequantize_rect(q, S, rows, cols, 1, 128, out);
+    free(q); free(S);
+    return 0;
 }
 
 /* FP8 block -> BF16 -> MXFP8 re-quantization [MX-adapter, 实现拆解 item 5:

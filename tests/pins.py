@@ -362,14 +362,17 @@ def pin_mx_roundtrip(orc, x):
 # block-FP8 and NVFP4 pins
 # ---------------------------------------------------------------------------
 
-def torch_blockfp8(x: np.ndarray, blk: int):
-    """Block-FP8 written with torch ops: fp32 amax / 448 per tile, fp32 x / S,
-    clamp to +-448 and torch's E4M3 cast; zero tiles divide by 1."""
+def torch_blockfp8(x: np.ndarray, blk: int, bc: int | None = None):
+    """Block-FP8 written with torch ops over blk x bc tiles (square unless bc is
+    given): fp32 amax / 448 per tile, fp32 x / S, clamp to +-448 and torch's
+    E4M3 cast; zero tiles divide by 1."""
+    br = blk
+    bc = blk if bc is None else bc
     rows, cols = x.shape
-    pr, pc = -(-rows // blk) * blk, -(-cols // blk) * blk
+    pr, pc = -(-rows // br) * br, -(-cols // bc) * bc
     xf = torch.zeros((pr, pc), dtype=torch.float32)
     xf[:rows, :cols] = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
-    tiles = xf.reshape(pr // blk, blk, pc // blk, blk)
+    tiles = xf.reshape(pr // br, br, pc // bc, bc)
     amax = tiles.abs().amax(dim=(1, 3))
     S = amax / 448.0
     div = torch.where(amax == 0, torch.ones_like(S), S)
@@ -377,6 +380,27 @@ def torch_blockfp8(x: np.ndarray, blk: int):
     q = t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
     q = q.reshape(pr, pc)[:rows, :cols].numpy()
     return q, S.numpy()
+
+
+def pin_blockfp8_1x128(orc, x):
+    """1 x 128 activation blocks: torch composition, the row-group max maps to
+    0x7E, dequantization via torch products, fake quant = dequant(quant)."""
+    q, S = orc.blockfp8_quantize_rect(x, 1, 128)
+    rq, rS = torch_blockfp8(x, 1, 128)
+    assert np.array_equal(S.view(np.uint32), rS.view(np.uint32))
+    assert np.array_equal(q, rq)
+    rows, cols = x.shape
+    mag = x.astype(np.int64) & 0x7FFF
+    for j in range(S.shape[1]):
+        blk = mag[:, 128 * j:128 * j + 128]
+        r = np.nonzero(blk.max(axis=1) > 0)[0]
+        c = np.argmax(blk[r], axis=1) + 128 * j
+        assert np.all((q[r, c] & 0x7F) == 0x7E)
+    dq = orc.blockfp8_dequantize_rect(q, S, 1, 128)
+    Sx = np.repeat(S, 128, axis=1)[:, :cols]
+    v = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).float() * torch.from_numpy(Sx)
+    assert np.array_equal(dq, v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(orc.blockfp8_fake_quant_1x128(x), dq)
 
 
 def pin_blockfp8(orc, x, blk=128):

@@ -36,6 +36,8 @@ MUTANTS = [
     ("colwise_t scale index", "st[c * nrg + j] = s[j * cols + c];", "st[c * nrg + j] = s[c];"),
     ("requant skips the bf16 rounding", "    orc_blockfp8_dequantize(q, scale, rows, cols, blk, bf);\n    orc_mxfp8_quantize_rowwise(bf, rows, cols, q8, scale8);",
      "    orc_blockfp8_dequantize(q, scale, rows, cols, blk, bf);\n    for (int64_t i = 0; i < rows * cols; ++i) bf[i] = (uint16_t)(bf[i] & 0xFFF0);\n    orc_mxfp8_quantize_rowwise(bf, rows, cols, q8, scale8);"),
+    ("rect tiles index rows by bc", "float S = scale[(r / br) * tc + c / bc];",
+     "float S = scale[(r / bc) * tc + c / bc];"),
     ("colwise group stride", "q[(r0 + i) * cols + c] = mx_encode(g[i], s);",
      "q[(r0 + i) * cols + c] = mx_encode(g[i], (uint8_t)(s + (i == 31)));"),
     ("blockfp8 divisor 447", "S = (float)amax / 448.0f;", "S = (float)amax / 447.0f;"),
@@ -90,6 +92,9 @@ def all_pins(orc):
     pins.pin_blockfp8(orc, z, 128)
     pins.pin_nvfp4(orc, workloads.random_bf16((64, 256), 21))
     pins.pin_requant_pow2_tiles(orc)
+    y = workloads.random_bf16((33, 200), 533)
+    y[3, :128] = 0
+    pins.pin_blockfp8_1x128(orc, y)
     pins.pin_requant_matches_steps(orc, workloads.random_bf16((200, 384), 17))
     pins.pin_mx4_sweep(orc, scale_bytes=list(range(0, 20)) + list(range(20, 253, 13)))
     pins.pin_mx4_nonfinite(orc)

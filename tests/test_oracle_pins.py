@@ -191,3 +191,14 @@ def test_requant_pow2_tiles_keep_codes(orc):
 def test_requant_matches_steps(orc, which):
     x = workloads.random_bf16((200, 384), 17) if which == "normal" else workloads.square_8192(n=256)
     pins.pin_requant_matches_steps(orc, x)
+
+
+@pytest.mark.parametrize("shape", [(64, 384), (33, 200), (1, 128), (17, 7168)])
+def test_blockfp8_1x128(orc, shape):
+    x = workloads.random_bf16(shape, 500 + shape[0])
+    x[3 % shape[0], :128] = 0                         # one all-zero group
+    pins.pin_blockfp8_1x128(orc, x)
+
+
+def test_blockfp8_1x128_t3(orc):
+    pins.pin_blockfp8_1x128(orc, workloads.act_16384(rows=64))
