@@ -132,6 +132,7 @@ def main():
                 "fq": torch.empty((rows, cols), dtype=torch.bfloat16, device=dev),
                 "qt": torch.empty((cols, rows), dtype=torch.uint8, device=dev),
                 "st": torch.empty((cols, (rows + 31) // 32), dtype=torch.uint8, device=dev),
+                "S1": torch.empty((rows, cols // 128), dtype=torch.float32, device=dev),
                 "q4": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
                 "s4": torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)}
 
@@ -273,6 +274,16 @@ def main():
             [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]), rows,
                                                           P(d["st"]), None, None, None, sp),
                                "colwise_t") for d in batches], 2 * e + e + e // 32)
+        # 1 x 128 block-FP8 (activation recipe) and its simulate-QAT
+        b1 = 2 * e + e + 4 * (e // 128)
+        breakdown["act_16384 block-FP8 1x128 quantize"] = rotated(
+            [lambda d=d: check(lib.blockfp8_quantize_1x128(P(d["x"]), rows, cols, P(d["qr"]),
+                                                           P(d["S1"]), None, sp), "bfp8 1x128")
+             for d in batches], b1)
+        breakdown["act_16384 block-FP8 1x128 simulate-QAT (fake-quant only)"] = rotated(
+            [lambda d=d: check(lib.blockfp8_fake_quant_1x128(P(d["x"]), rows, cols, P(d["fq"]),
+                                                             sp), "bfp8 1x128 fq")
+             for d in batches], 4 * e)
         # MXFP4 on the same batches: quantize, simulate-QAT, dequantize
         m4 = 2 * e + e // 2 + e // 32
         breakdown["act_16384 MXFP4 quantize"] = rotated(

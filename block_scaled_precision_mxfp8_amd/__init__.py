@@ -52,6 +52,9 @@ SIGNATURES = {
     "mxq_quantize_rowwise_grouped": (ctypes.c_int, [_vp, _i32, _vp, _sz, _vp]),
     "blockfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "blockfp8_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "blockfp8_quantize_1x128": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "blockfp8_dequantize_1x128": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "blockfp8_fake_quant_1x128": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "blockfp8_to_mxfp8": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "mxfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "mxfp4_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
@@ -331,6 +334,44 @@ def mxfp4_simulate_qat(x: torch.Tensor) -> torch.Tensor:
     out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x2.device)
     st = load().mxfp4_fake_quant(_ptr(x2), rows, cols, _ptr(out), _stream(x2))
     _check("mxfp4_fake_quant", st)
+    return out.view(x.shape)
+
+
+def blockfp8_quantize_1x128(x: torch.Tensor, fake_quant: bool = False):
+    """1 x 128 block-FP8 of a [..., cols] bf16 tensor flattened to 2-D: (q uint8
+    [rows, cols], S float32 [rows, ceil(cols/128)]) and, with fake_quant, the
+    bf16 dequantization as a third tensor."""
+    _need_bf16_cuda(x)
+    x = _as_2d_rows(x).contiguous()
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    S = torch.empty((rows, (cols + 127) // 128), dtype=torch.float32, device=x.device)
+    fq = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device) if fake_quant else None
+    st = load().blockfp8_quantize_1x128(_ptr(x), rows, cols, _ptr(q), _ptr(S), _ptr(fq), _stream(x))
+    _check("blockfp8_quantize_1x128", st)
+    return (q, S, fq) if fake_quant else (q, S)
+
+
+def blockfp8_dequantize_1x128(q: torch.Tensor, S: torch.Tensor) -> torch.Tensor:
+    q = q.contiguous()
+    S = S.contiguous()
+    rows, cols = q.shape
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=q.device)
+    st = load().blockfp8_dequantize_1x128(_ptr(q.view(torch.uint8)), _ptr(S), rows, cols,
+                                          _ptr(out), _stream(q))
+    _check("blockfp8_dequantize_1x128", st)
+    return out
+
+
+def fp8_simulate_qat(x: torch.Tensor) -> torch.Tensor:
+    """1 x 128 block-FP8 fake quantization of a [..., cols] bf16 tensor (bf16
+    of the same shape)."""
+    _need_bf16_cuda(x)
+    x2 = _as_2d_rows(x).contiguous()
+    rows, cols = x2.shape
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=x2.device)
+    st = load().blockfp8_fake_quant_1x128(_ptr(x2), rows, cols, _ptr(out), _stream(x2))
+    _check("blockfp8_fake_quant_1x128", st)
     return out.view(x.shape)
 
 

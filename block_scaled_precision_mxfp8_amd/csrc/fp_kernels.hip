@@ -31,6 +31,33 @@ constexpr bool kNTLoadDq = false;
 constexpr bool kNTLoadNvAmax = false;
 constexpr bool kNTLoadNvQuant = true;
 
+// 8 bf16 -> 8 E4M3 codes of fl32(x / div): by reciprocal + FMA correction
+// when `fast` (the divisor is in the exact domain), else by IEEE division;
+// all NaN with each element's sign for a NaN/Inf block.
+__device__ __forceinline__ uint2 bfp8_encode8(uint4 v, float div, float y, bool fast,
+                                              bool nonfinite)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t c[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w0 = w[2 * h], w1 = w[2 * h + 1];
+        const float f0 = bf16lo_to_f32(w0), f1 = bf16hi_to_f32(w0);
+        const float f2 = bf16lo_to_f32(w1), f3 = bf16hi_to_f32(w1);
+        if (nonfinite) {
+            c[h] = 0x7F7F7F7Fu | signs4(w0, w1);
+        } else if (fast) {
+            c[h] = cvt_fp8x2_f32<true>(cvt_fp8x2_f32<false>(0u, div_markstein(f0, div, y),
+                                                            div_markstein(f1, div, y)),
+                                       div_markstein(f2, div, y), div_markstein(f3, div, y));
+        } else {
+            c[h] = cvt_fp8x2_f32<true>(cvt_fp8x2_f32<false>(0u, f0 / div, f1 / div), f2 / div,
+                                       f3 / div);   // IEEE fp32 divisions
+        }
+    }
+    return make_uint2(c[0], c[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Block-FP8: one workgroup per 128 x 128 tile.  Thread t loads 8 rows
 // (t/16 + 16k) x 8 columns ((t%16)*8): each wave load covers 4 rows x 256 B.
@@ -75,25 +102,8 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int64_t r = rbase + 16 * k;
-        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-        uint32_t c[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t w0 = w[2 * h], w1 = w[2 * h + 1];
-            const float f0 = bf16lo_to_f32(w0), f1 = bf16hi_to_f32(w0);
-            const float f2 = bf16lo_to_f32(w1), f3 = bf16hi_to_f32(w1);
-            if (nonfinite) {
-                c[h] = 0x7F7F7F7Fu | signs4(w0, w1);
-            } else if (fast) {
-                c[h] = cvt_fp8x2_f32<true>(cvt_fp8x2_f32<false>(0u, div_markstein(f0, div, y),
-                                                                div_markstein(f1, div, y)),
-                                           div_markstein(f2, div, y), div_markstein(f3, div, y));
-            } else {
-                c[h] = cvt_fp8x2_f32<true>(cvt_fp8x2_f32<false>(0u, f0 / div, f1 / div),
-                                           f2 / div, f3 / div);   // IEEE fp32 divisions
-            }
-        }
-        if (cin && r < rows) st8<kNTStore>(q + r * cols + col, make_uint2(c[0], c[1]));
+        const uint2 c = bfp8_encode8(v[k], div, y, fast, nonfinite);
+        if (cin && r < rows) st8<kNTStore>(q + r * cols + col, c);
     }
 }
 
@@ -140,8 +150,10 @@ __device__ __forceinline__ uint4 bfp8_dequant8(uint2 c, float S, bool slow)
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Tiles: 512-column segment x 32 rows (4 waves x 8 rows); a 32-row block lies
-// inside one 128-row tile row, so each lane needs one scale.
+// Tiles: 512-column segment x 32 rows (4 waves x 8 rows).  128 x 128 blocks
+// (kRowScales false): a 32-row block lies inside one 128-row tile row, so each
+// lane needs one scale; 1 x 128 blocks (kRowScales true): one scale per row.
+template <bool kRowScales>
 __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__restrict__ q,
                                                            const float *__restrict__ scale,
                                                            int64_t rows, int64_t cols,
@@ -156,25 +168,94 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
     const int64_t col = seg * kSegNv + lane * 8;
     if (col >= cols) return;  // cols % 8 == 0; no barriers below
     const int64_t r0 = rb * kRowsNv + wave;
-    const float S = scale[((rb * kRowsNv) / kBlk) * tc + col / kBlk];
     constexpr int kR = kRowsNv / 4;
+    float S[kR];
     uint2 c[kR];
-    bool nan_code = false;
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
         c[i] = make_uint2(0, 0);
+        S[i] = 0.0f;
+        if (kRowScales) {
+            if (r < rows) S[i] = scale[r * tc + col / kBlk];
+        } else {
+            S[i] = i == 0 ? scale[((rb * kRowsNv) / kBlk) * tc + col / kBlk] : S[0];
+        }
         if (r < rows) c[i] = ld8<kNTLoadDq>(q + r * cols + col);
         const uint32_t tx = c[i].x & 0x7F7F7F7Fu, ty = c[i].y & 0x7F7F7F7Fu;
-        nan_code |= (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
+        // NaN products (NaN code, NaN or infinite scale) take the exact sign rule
+        bad |= (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
+        bad |= !__builtin_isfinite(S[i]);
     }
-    // NaN products (NaN code, NaN or infinite scale) take the exact sign rule
-    const bool slow = wave_any(nan_code || !__builtin_isfinite(S));
+    const bool slow = wave_any(bad);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
-        const uint4 o = slow ? bfp8_dequant8(c[i], S, true) : bfp8_dequant8(c[i], S, false);
+        const uint4 o = slow ? bfp8_dequant8(c[i], S[i], true) : bfp8_dequant8(c[i], S[i], false);
         if (r < rows) st16<kNTStore>(out + r * cols + col, o);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-FP8 with 1 x 128 blocks (the activation recipe; with kFQ the fake
+// quantization fp8_simulate_qat(x, 128)).  Tiles as the dequantizer; 16
+// lanes (8 columns each) hold one block of a row, reduced with 4 DPP steps.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t row16_max(uint32_t v)
+{
+    v = quad_max(v);
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // half mirror
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // mirror
+}
+
+template <bool kQ, bool kFQ>
+__global__ __launch_bounds__(256) void bfp8_1x128_kernel(const uint16_t *__restrict__ x,
+                                                         int64_t rows, int64_t cols,
+                                                         uint8_t *__restrict__ q,
+                                                         float *__restrict__ scale,
+                                                         uint16_t *__restrict__ fq, int64_t tc,
+                                                         int64_t nseg)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSegNv + lane * 8;
+    const bool cin = col < cols;  // cols % 8 == 0; lanes past the edge still join the DPP
+    const int64_t r0 = rb * kRowsNv + wave;
+    constexpr int kR = kRowsNv / 4;
+    uint4 v[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (cin && r < rows) v[i] = ld16<kNTLoad>(x + r * cols + col);
+    }
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        const bool ok = cin && r < rows;
+        const uint32_t m = row16_max(amax8(v[i]));
+        const bool nonfinite = m >= 0x7F80u;
+        const float A = __uint_as_float(m << 16);      // exact: amax is a bf16 value
+        const float S = nonfinite ? __builtin_nanf("") : A / 448.0f;
+        const float div = (m == 0u) ? 1.0f : S;        // zero block: codes are +-0
+        const bool fast = !nonfinite && markstein_ok(div);
+        const bool wave_fast = !wave_any(!fast);
+        const float y = fast ? 1.0f / div : 0.0f;
+        const uint2 c = wave_fast ? bfp8_encode8(v[i], div, y, true, false)
+                                  : bfp8_encode8(v[i], div, y, fast, nonfinite);
+        if (kQ && ok) {
+            st8<kNTStore>(q + r * cols + col, c);
+            scale[r * tc + col / kBlk] = S;  // the same value from the block's 16 lanes
+        }
+        if (kFQ) {
+            const bool slow = wave_any(nonfinite);
+            const uint4 d = slow ? bfp8_dequant8(c, S, true) : bfp8_dequant8(c, S, false);
+            if (ok) st16<kNTStore>(fq + r * cols + col, d);
+        }
     }
 }
 
@@ -453,15 +534,40 @@ hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint
 }
 
 hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
-                               uint16_t *out, hipStream_t stream)
+                               bool row_scales, uint16_t *out, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
     const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const int64_t tc = (cols + kBlk - 1) / kBlk;
-    hipLaunchKernelGGL(bfp8_dequant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scale,
-                       rows, cols, out, tc, nseg);
+    if (row_scales)
+        hipLaunchKernelGGL((bfp8_dequant_kernel<true>), dim3((unsigned)tiles), dim3(256), 0,
+                           stream, q, scale, rows, cols, out, tc, nseg);
+    else
+        hipLaunchKernelGGL((bfp8_dequant_kernel<false>), dim3((unsigned)tiles), dim3(256), 0,
+                           stream, q, scale, rows, cols, out, tc, nseg);
+    return hipGetLastError();
+}
+
+hipError_t launch_bfp8_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                             float *scale, uint16_t *fq, hipStream_t stream)
+{
+    const int64_t tc = (cols + kBlk - 1) / kBlk;
+    const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
+    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    if (tiles <= 0) return hipSuccess;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)tiles), block(256);
+    if (q && fq)
+        hipLaunchKernelGGL((bfp8_1x128_kernel<true, true>), grid, block, 0, stream, x, rows, cols,
+                           q, scale, fq, tc, nseg);
+    else if (q)
+        hipLaunchKernelGGL((bfp8_1x128_kernel<true, false>), grid, block, 0, stream, x, rows, cols,
+                           q, scale, fq, tc, nseg);
+    else
+        hipLaunchKernelGGL((bfp8_1x128_kernel<false, true>), grid, block, 0, stream, x, rows, cols,
+                           q, scale, fq, tc, nseg);
     return hipGetLastError();
 }
 

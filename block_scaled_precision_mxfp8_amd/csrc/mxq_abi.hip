@@ -265,7 +265,45 @@ mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t row
     if (!q || !scale || !out) return MXQ_EINVAL;
     if (!aligned(q, 8) || !aligned(out, 16) || !aligned(scale, 4)) return MXQ_EALIGN;
     if (!fits(rows, cols)) return MXQ_ESIZE;
-    return from_hip(mxq::launch_bfp8_dequant(q, scale, rows, cols, out, as_stream(stream)));
+    return from_hip(mxq::launch_bfp8_dequant(q, scale, rows, cols, false, out, as_stream(stream)));
+}
+
+mxq_status blockfp8_quantize_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                                   float *scale, uint16_t *fq, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 8 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !q || !scale) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4) || (fq && !aligned(fq, 16)))
+        return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_1x128(x, rows, cols, q, scale, fq, as_stream(stream)));
+}
+
+mxq_status blockfp8_dequantize_1x128(const uint8_t *q, const float *scale, int64_t rows,
+                                     int64_t cols, uint16_t *out, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 8 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!q || !scale || !out) return MXQ_EINVAL;
+    if (!aligned(q, 8) || !aligned(out, 16) || !aligned(scale, 4)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_dequant(q, scale, rows, cols, true, out, as_stream(stream)));
+}
+
+mxq_status blockfp8_fake_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
+                                     uint16_t *out, void *stream)
+{
+    if (rows < 0 || cols < 0) return MXQ_EINVAL;
+    if (cols % 8 != 0) return MXQ_ESHAPE;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!x || !out) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(out, 16)) return MXQ_EALIGN;
+    if (!fits(rows, cols)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_1x128(x, rows, cols, nullptr, nullptr, out,
+                                           as_stream(stream)));
 }
 
 mxq_status blockfp8_to_mxfp8(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,

@@ -191,6 +191,32 @@ mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t row
                                int32_t blk, uint16_t *out, void *stream);
 
 /*
+ * Block-FP8 with 1 x 128 blocks along each row (the activation recipe):
+ * per block of 128 consecutive values of a row (the last one shorter when
+ * cols % 128 != 0), S = fl32(amax / 448) and q = E4M3_RNE_sat(fl32(x / S)),
+ * with the same zero-block and non-finite rules as blockfp8_quantize.
+ *   x      [rows, cols] bf16, contiguous, 16-byte aligned
+ *   q      [rows, cols] E4M3 codes, contiguous, 8-byte aligned
+ *   scale  [rows, ceil(cols/128)] fp32, 4-byte aligned
+ *   fq     optional [rows, cols] bf16 = blockfp8_dequantize_1x128(q, scale),
+ *          16-byte aligned; NULL to skip
+ * Shape: cols % 8 == 0.
+ */
+mxq_status blockfp8_quantize_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                                   float *scale, uint16_t *fq, void *stream);
+
+/* 1 x 128 block-FP8 dequantization: out = bf16_RNE(fl32(E4M3(q) * S)); a NaN
+ * product gives the quiet NaN with the code's sign.  Shapes as above. */
+mxq_status blockfp8_dequantize_1x128(const uint8_t *q, const float *scale, int64_t rows,
+                                     int64_t cols, uint16_t *out, void *stream);
+
+/* Fake quantization fp8_simulate_qat(x, 128) (miles PR #1372 "V4 mxfp4", the
+ * compressor review; fp32 scales per its PR description): out =
+ * blockfp8_dequantize_1x128(blockfp8_quantize_1x128(x)) in one pass. */
+mxq_status blockfp8_fake_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
+                                     uint16_t *out, void *stream);
+
+/*
  * FP8 block -> BF16 -> MXFP8 re-quantization in one pass: the conversion of
  * a block-FP8 checkpoint to MXFP8 ("PR #1935 完整报告", 实现拆解 item 5,
  * the FP8->BF16->MXFP8 conversion).  The result equals

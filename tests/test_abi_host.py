@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                  "nvfp4_quantize", "nvfp4_dequantize", "mxq_status_string", "mxq_abi_version",
                  "mxq_grouped_workspace_size", "nvfp4_workspace_size", "mxfp4_quantize",
                  "mxfp4_dequantize", "mxfp4_fake_quant", "mxq_quantize_colwise_t",
-                 "blockfp8_to_mxfp8"]:
+                 "blockfp8_to_mxfp8", "blockfp8_quantize_1x128", "blockfp8_dequantize_1x128",
+                 "blockfp8_fake_quant_1x128"]:
         assert want in names
     assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
 
@@ -185,6 +186,28 @@ def test_blockfp8_to_mxfp8_errors(lib):
     assert f(NULL, NULL, 0, 32, 128, NULL, NULL, NULL) == mxq.MXQ_OK
 
 
+def test_blockfp8_1x128_errors(lib):
+    f = lib.blockfp8_quantize_1x128
+    assert f(P16, -1, 32, P16, P16, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 36, P16, P16, NULL, NULL) == mxq.MXQ_ESHAPE           # cols % 8
+    assert f(NULL, 4, 32, P16, P16, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, NULL, P16, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, P16, NULL, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P8, 4, 32, P16, P16, NULL, NULL) == mxq.MXQ_EALIGN
+    assert f(P16, 4, 32, P4, P16, NULL, NULL) == mxq.MXQ_EALIGN            # q 8-aligned
+    assert f(P16, 4, 32, P16, P2, NULL, NULL) == mxq.MXQ_EALIGN            # scale 4-aligned
+    assert f(P16, 4, 32, P16, P16, P8, NULL) == mxq.MXQ_EALIGN             # fq 16-aligned
+    assert f(NULL, 0, 32, NULL, NULL, NULL, NULL) == mxq.MXQ_OK
+    d = lib.blockfp8_dequantize_1x128
+    assert d(P16, P16, 4, 36, P16, NULL) == mxq.MXQ_ESHAPE
+    assert d(P16, NULL, 4, 32, P16, NULL) == mxq.MXQ_EINVAL
+    assert d(P16, P16, 4, 32, P8, NULL) == mxq.MXQ_EALIGN
+    fq = lib.blockfp8_fake_quant_1x128
+    assert fq(P16, 4, 32, NULL, NULL) == mxq.MXQ_EINVAL
+    assert fq(P2, 4, 32, P16, NULL) == mxq.MXQ_EALIGN
+    assert fq(P16, 4, 12, P16, NULL) == mxq.MXQ_ESHAPE
+
+
 def test_mxfp4_errors(lib):
     f = lib.mxfp4_quantize
     assert f(P16, -1, 32, P16, P16, NULL, NULL) == mxq.MXQ_EINVAL
@@ -214,7 +237,8 @@ def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros((4, 32), dtype=torch.bfloat16)
     for fn in (mxq.quantize_rowwise, mxq.fake_quant, mxq.blockfp8_quantize, mxq.nvfp4_quantize,
-               mxq.mxfp8_quantize, mxq.mxfp4_quantize, mxq.mxfp4_simulate_qat):
+               mxq.mxfp8_quantize, mxq.mxfp4_quantize, mxq.mxfp4_simulate_qat,
+               mxq.blockfp8_quantize_1x128, mxq.fp8_simulate_qat):
         with pytest.raises(ValueError):
             fn(x)
     with pytest.raises(TypeError):
