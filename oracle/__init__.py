@@ -110,6 +110,11 @@ class Oracle:
         L.orc_blockfp8_to_mxfp8.restype = ctypes.c_int
         L.orc_nvfp4_quantize.argtypes = [_u16p, _i64, _i64, _u8p, _u8p, _f32p]
         L.orc_nvfp4_quantize.restype = None
+        L.orc_nvfp4_quantize_grouped.argtypes = [ctypes.c_int32, ctypes.POINTER(_u16p),
+                                                 ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                                 ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                                 ctypes.POINTER(_u8p), ctypes.POINTER(_u8p), _f32p]
+        L.orc_nvfp4_quantize_grouped.restype = ctypes.c_int
         L.orc_nvfp4_dequantize.argtypes = [_u8p, _u8p, _f32p, _i64, _i64, _u16p]
         L.orc_nvfp4_dequantize.restype = None
         self.L = L
@@ -299,6 +304,24 @@ class Oracle:
         g = np.empty((1,), np.float32)
         self.L.orc_nvfp4_quantize(_p(x, _u16p), rows, cols, _p(q, _u8p), _p(s, _u8p), _p(g, _f32p))
         return q, s, g
+
+    def nvfp4_quantize_grouped(self, xs, groups, n_groups: int):
+        """NVFP4 of each tensor in xs with the global scale shared within scale
+        groups (groups[i] is tensor i's group) -> ([(q_packed, s)], g float32
+        [n_groups])."""
+        xs = [_bits16(x) for x in xs]
+        n = len(xs)
+        outs = [(np.empty((x.shape[0], x.shape[1] // 2), np.uint8),
+                 np.empty((x.shape[0], x.shape[1] // 16), np.uint8)) for x in xs]
+        gs = np.empty((max(n_groups, 1),), np.float32)
+        arr = lambda ct, vals: (ct * n)(*vals)
+        rc = self.L.orc_nvfp4_quantize_grouped(
+            n, arr(_u16p, [_p(x, _u16p) for x in xs]), arr(_i64, [x.shape[0] for x in xs]),
+            arr(_i64, [x.shape[1] for x in xs]), arr(ctypes.c_int32, [int(g) for g in groups]),
+            int(n_groups), arr(_u8p, [_p(o[0], _u8p) for o in outs]),
+            arr(_u8p, [_p(o[1], _u8p) for o in outs]), _p(gs, _f32p))
+        assert rc == 0
+        return outs, gs[:n_groups]
 
     def nvfp4_dequantize(self, q: np.ndarray, s: np.ndarray, g: np.ndarray) -> np.ndarray:
         q = np.ascontiguousarray(q, dtype=np.uint8)

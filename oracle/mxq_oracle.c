@@ -554,19 +554,30 @@ int orc_blockfp8_to_mxfp8(const uint8_t *q, const float *scale, int64_t rows, in
  * q_packed [rows, cols/2], s [rows, cols/16], global_scale[0] = g.
  * A tensor holding NaN or Inf: g = NaN, every scale byte 0x7F, every nibble
  * 0x7 | sign. */
-void orc_nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
-                        uint8_t *q_packed, uint8_t *s_e4m3, float *global_scale)
+/* max |x| over n bf16 values, and whether any of them is NaN or Inf. */
+static void nv_amax(const uint16_t *x, int64_t n, double *A, int *nonfinite)
 {
-    double A = 0.0;
-    int nonfinite = 0;
-    for (int64_t i = 0; i < rows * cols; ++i) {
+    for (int64_t i = 0; i < n; ++i) {
         double a = fabs(orc_bf16_to_double(x[i]));
-        if (!isfinite(a)) nonfinite = 1;
-        else if (a > A) A = a;
+        if (!isfinite(a)) *nonfinite = 1;
+        else if (a > *A) *A = a;
     }
+}
+
+/* The global scale g of an amax A (NaN when the values held NaN or Inf). */
+static float nv_global(double A, int nonfinite)
+{
+    if (nonfinite) return NAN;
+    float g = (float)A / 2688.0f;
+    return g;
+}
+
+/* The per-block steps of one tensor under a given global scale g. */
+static void nv_quantize_given(const uint16_t *x, int64_t rows, int64_t cols, float g,
+                              int nonfinite, uint8_t *q_packed, uint8_t *s_e4m3)
+{
     int64_t nb = cols / NV_BLOCK;
     if (nonfinite) {
-        global_scale[0] = NAN;
         for (int64_t i = 0; i < rows * nb; ++i) s_e4m3[i] = 0x7F;
         for (int64_t r = 0; r < rows; ++r)
             for (int64_t c = 0; c < cols; c += 2) {
@@ -576,8 +587,6 @@ void orc_nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
             }
         return;
     }
-    float g = (float)A / 2688.0f;
-    global_scale[0] = g;
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t k = 0; k < nb; ++k) {
             const uint16_t *src = x + r * cols + k * NV_BLOCK;
@@ -611,6 +620,41 @@ void orc_nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
                     (uint8_t)(nib[i] | (nib[i + 1] << 4));
         }
     }
+}
+
+void orc_nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
+                        uint8_t *q_packed, uint8_t *s_e4m3, float *global_scale)
+{
+    double A = 0.0;
+    int nonfinite = 0;
+    nv_amax(x, rows * cols, &A, &nonfinite);
+    float g = nv_global(A, nonfinite);
+    global_scale[0] = g;
+    nv_quantize_given(x, rows, cols, g, nonfinite, q_packed, s_e4m3);
+}
+
+/* NVFP4 of several tensors whose global scale is shared within caller-given
+ * scale groups: tensor i belongs to group[i] in [0, n_groups); A of a group is
+ * the max |x| over all its tensors (NaN/Inf in any of them makes the whole
+ * group non-finite), g = fl32(A / 2688) is written to gs[group], and every
+ * member is quantized with that g.  A group with no member gets g = 0.  This
+ * covers the two gate/up conventions of a fused gated-MoE weight [xorl PR #30,
+ * deep review item 3]: a global scale per half (gate and up in separate
+ * groups, the QAT form) and one shared weight_scale_2 (gate and up in one
+ * group, the export form). */
+int orc_nvfp4_quantize_grouped(int32_t n, const uint16_t *const *xs, const int64_t *rows,
+                               const int64_t *cols, const int32_t *group, int32_t n_groups,
+                               uint8_t *const *qs, uint8_t *const *ss, float *gs)
+{
+    double *A = (double *)calloc((size_t)n_groups, sizeof(double));
+    int *nf = (int *)calloc((size_t)n_groups, sizeof(int));
+    if (!A || !nf) { free(A); free(nf); return -1; }
+    for (int32_t i = 0; i < n; ++i) nv_amax(xs[i], rows[i] * cols[i], &A[group[i]], &nf[group[i]]);
+    for (int32_t j = 0; j < n_groups; ++j) gs[j] = nv_global(A[j], nf[j]);
+    for (int32_t i = 0; i < n; ++i)
+        nv_quantize_given(xs[i], rows[i], cols[i], gs[group[i]], nf[group[i]], qs[i], ss[i]);
+    free(A); free(nf);
+    return 0;
 }
 
 /* NVFP4 dequantization: bf16_RNE(fl32(E2M1(q) * eff)), eff = fl32(E4M3(s) * g).

@@ -650,3 +650,34 @@ def pin_requant_matches_steps(orc, x):
     q8, s8 = orc.blockfp8_to_mxfp8(q, S)
     rq, rs = orc.mxfp8_quantize_rowwise(bf)
     assert np.array_equal(q8, rq) and np.array_equal(s8, rs)
+
+
+def pin_nvfp4_grouped(orc, xs, groups, n_groups):
+    """Grouped NVFP4: each group's g is fl32(max over its members / 2688) (the
+    numpy composition), each member equals single-tensor NVFP4 of that member
+    after the group's largest value is planted into a copy of it (which makes
+    the single-tensor amax the group's, leaving every other block unchanged),
+    and a one-tensor group equals nvfp4_quantize exactly."""
+    outs, gs = orc.nvfp4_quantize_grouped(xs, groups, n_groups)
+    mags = [torch_bf16_values(x) for x in xs]
+    for j in range(n_groups):
+        members = [i for i in range(len(xs)) if groups[i] == j]
+        if not members:
+            assert gs[j] == 0
+            continue
+        A = np.float32(max(np.abs(mags[i]).max() for i in members))
+        assert gs[j].view(np.uint32) == np.float32(A / np.float32(2688.0)).view(np.uint32)
+        for i in members:
+            q, s = outs[i]
+            if len(members) == 1:
+                rq, rs, rg = orc.nvfp4_quantize(xs[i])
+                assert np.array_equal(q, rq) and np.array_equal(s, rs)
+                continue
+            # plant the group max into an extra block-aligned row of this member
+            x = xs[i]
+            amax_bits = max((xs[k].astype(np.int64) & 0x7FFF).max() for k in members)
+            extra = np.zeros((1, x.shape[1]), np.uint16)
+            extra[0, 0] = amax_bits
+            rq, rs, rg = orc.nvfp4_quantize(np.concatenate([x, extra]))
+            assert rg.view(np.uint32)[0] == gs[j].view(np.uint32)
+            assert np.array_equal(q, rq[:-1]) and np.array_equal(s, rs[:-1])

@@ -38,6 +38,9 @@ MUTANTS = [
      "    orc_blockfp8_dequantize(q, scale, rows, cols, blk, bf);\n    for (int64_t i = 0; i < rows * cols; ++i) bf[i] = (uint16_t)(bf[i] & 0xFFF0);\n    orc_mxfp8_quantize_rowwise(bf, rows, cols, q8, scale8);"),
     ("rect tiles index rows by bc", "float S = scale[(r / br) * tc + c / bc];",
      "float S = scale[(r / bc) * tc + c / bc];"),
+    ("nvfp4 group amax over the first member only",
+     "for (int32_t i = 0; i < n; ++i) nv_amax(xs[i], rows[i] * cols[i], &A[group[i]], &nf[group[i]]);",
+     "for (int32_t i = 0; i < n; ++i) if (A[group[i]] == 0.0) nv_amax(xs[i], rows[i] * cols[i], &A[group[i]], &nf[group[i]]);"),
     ("colwise group stride", "q[(r0 + i) * cols + c] = mx_encode(g[i], s);",
      "q[(r0 + i) * cols + c] = mx_encode(g[i], (uint8_t)(s + (i == 31)));"),
     ("blockfp8 divisor 447", "S = (float)amax / 448.0f;", "S = (float)amax / 447.0f;"),
@@ -92,6 +95,8 @@ def all_pins(orc):
     pins.pin_blockfp8(orc, z, 128)
     pins.pin_nvfp4(orc, workloads.random_bf16((64, 256), 21))
     pins.pin_requant_pow2_tiles(orc)
+    hx = [workloads.random_bf16((32, 64), 600 + i, std=0.02 * (1 + i)) for i in range(4)]
+    pins.pin_nvfp4_grouped(orc, hx, [0, 0, 1, 1], 3)
     y = workloads.random_bf16((33, 200), 533)
     y[3, :128] = 0
     pins.pin_blockfp8_1x128(orc, y)

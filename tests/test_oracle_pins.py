@@ -202,3 +202,34 @@ def test_blockfp8_1x128(orc, shape):
 
 def test_blockfp8_1x128_t3(orc):
     pins.pin_blockfp8_1x128(orc, workloads.act_16384(rows=64))
+
+
+def _moe_halves(seed):
+    rng = np.random.default_rng(seed)
+    xs = []
+    for e in range(3):
+        gate = workloads.random_bf16((32, 64), seed + 10 * e, std=0.02 * (1 + e))
+        up = workloads.random_bf16((32, 64), seed + 10 * e + 1, std=0.05 * (1 + e))
+        xs += [gate, up]
+    return xs
+
+
+def test_nvfp4_grouped_per_half(orc):
+    """Per-half global scales (QAT form): each gate and each up its own group."""
+    xs = _moe_halves(70)
+    pins.pin_nvfp4_grouped(orc, xs, list(range(len(xs))), len(xs))
+
+
+def test_nvfp4_grouped_shared_gate_up(orc):
+    """One shared global scale per expert's gate and up (export form), plus an
+    unused group."""
+    xs = _moe_halves(80)
+    pins.pin_nvfp4_grouped(orc, xs, [i // 2 for i in range(len(xs))], len(xs) // 2 + 1)
+
+
+def test_nvfp4_grouped_nonfinite_member(orc):
+    xs = _moe_halves(90)
+    xs[3][5, 7] = 0x7FC0
+    outs, gs = orc.nvfp4_quantize_grouped(xs, [i // 2 for i in range(len(xs))], 3)
+    assert np.isnan(gs[1]) and np.isfinite(gs[0]) and np.isfinite(gs[2])
+    assert np.all(outs[2][1] == 0x7F) and np.all(outs[3][1] == 0x7F)
