@@ -346,7 +346,32 @@ def main():
         breakdown["moe_experts grouped row-wise"] = rotated(
             [lambda: check(lib.mxq_quantize_rowwise_grouped(descs, len(xs), P(gws), wsz, sp),
                            "grouped")], 3 * ge + ge // 32, iters=10)
-        del xs, outs, gws
+        del outs, gws
+        torch.cuda.empty_cache()
+        # NVFP4 of the 256 gate/up tensors in one grouped call, gate and up of
+        # an expert sharing one global scale (the exported weight_scale_2)
+        gu = [i for i, (name, _, _) in enumerate(shapes)
+              if name.endswith(("gate_proj.weight", "up_proj.weight"))]
+        assert len(gu) == 2 * (len(shapes) // 3)
+        nvd = (mxq.NvGroupDesc * len(gu))()
+        nv_outs = []
+        for k, i in enumerate(gu):
+            t = xs[i]
+            q_ = torch.empty((t.shape[0], t.shape[1] // 2), dtype=torch.uint8, device=dev)
+            s_ = torch.empty((t.shape[0], t.shape[1] // 16), dtype=torch.uint8, device=dev)
+            nv_outs.append((q_, s_))
+            nvd[k] = mxq.NvGroupDesc(t.data_ptr(), q_.data_ptr(), s_.data_ptr(), t.shape[0],
+                                     t.shape[1], i // 3, 0)
+        n_exp = len(shapes) // 3
+        nvg = torch.empty((n_exp,), dtype=torch.float32, device=dev)
+        nvw_n = lib.nvfp4_grouped_workspace_size(nvd, len(gu))
+        nvw = torch.empty((nvw_n,), dtype=torch.uint8, device=dev)
+        gue = sum(xs[i].numel() for i in gu)
+        breakdown["moe gate/up NVFP4 grouped, shared scale per expert (unique bytes)"] = rotated(
+            [lambda: check(lib.nvfp4_quantize_grouped(nvd, len(gu), P(nvg), n_exp, P(nvw), nvw_n,
+                                                      sp), "nvfp4 grouped")],
+            2 * gue + gue // 2 + gue // 16 + 4 * n_exp, iters=10)
+        del xs, nv_outs, nvw
         torch.cuda.empty_cache()
 
         # square [8192, 8192]: block-FP8 and NVFP4, quantize and dequantize

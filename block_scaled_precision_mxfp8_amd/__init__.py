@@ -62,6 +62,8 @@ SIGNATURES = {
     "nvfp4_workspace_size": (_sz, []),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
+    "nvfp4_grouped_workspace_size": (_sz, [_vp, _i32]),
+    "nvfp4_quantize_grouped": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _sz, _vp]),
 }
 
 
@@ -69,6 +71,12 @@ class GroupDesc(ctypes.Structure):
     """mxq_group_desc."""
     _fields_ = [("x", _vp), ("q", _vp), ("scale", _vp), ("rows", _i64), ("cols", _i64),
                 ("ldx", _i64), ("ldq", _i64), ("lds", _i64)]
+
+
+class NvGroupDesc(ctypes.Structure):
+    """nvfp4_group_desc."""
+    _fields_ = [("x", _vp), ("q", _vp), ("s", _vp), ("rows", _i64), ("cols", _i64),
+                ("scale_group", _i32), ("reserved", _i32)]
 
 
 class MXQError(RuntimeError):
@@ -414,6 +422,43 @@ def nvfp4_quantize(x: torch.Tensor, workspace: torch.Tensor | None = None):
                                workspace.numel() * workspace.element_size(), _stream(x))
     _check("nvfp4_quantize", st)
     return q, s, g
+
+
+def nvfp4_quantize_grouped(xs, groups, n_groups: int, workspace: torch.Tensor | None = None):
+    """NVFP4 of every 2-D bf16 tensor in xs in one call, the global scale shared
+    within scale groups (groups[i] is tensor i's group).  Returns
+    ([(q, s), ...], g float32 [n_groups])."""
+    if len(xs) != len(groups):
+        raise ValueError("one scale group per tensor")
+    if n_groups < 1:
+        raise ValueError("n_groups must be >= 1")
+    dev = None
+    for x in xs:
+        _need_bf16_cuda(x)
+        if x.dim() != 2:
+            raise ValueError("nvfp4_quantize_grouped expects 2-D tensors")
+        dev = x.device
+    xs = [x.contiguous() for x in xs]
+    if dev is None:
+        raise ValueError("no tensors")
+    outs = [(torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev),
+             torch.empty((x.shape[0], x.shape[1] // NV_BLOCK), dtype=torch.uint8, device=dev))
+            for x in xs]
+    gs = torch.empty((n_groups,), dtype=torch.float32, device=dev)
+    descs = (NvGroupDesc * len(xs))()
+    for i, (x, (q, s)) in enumerate(zip(xs, outs)):
+        empty = x.numel() == 0
+        descs[i] = NvGroupDesc(None if empty else x.data_ptr(), None if empty else q.data_ptr(),
+                               None if empty else s.data_ptr(), x.shape[0], x.shape[1],
+                               int(groups[i]), 0)
+    L = load()
+    nbytes = L.nvfp4_grouped_workspace_size(descs, len(xs))
+    if workspace is None:
+        workspace = torch.empty((max(int(nbytes), 16),), dtype=torch.uint8, device=dev)
+    st = L.nvfp4_quantize_grouped(descs, len(xs), _ptr(gs), n_groups, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(xs[0]))
+    _check("nvfp4_quantize_grouped", st)
+    return outs, gs
 
 
 def nvfp4_dequantize(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor) -> torch.Tensor:

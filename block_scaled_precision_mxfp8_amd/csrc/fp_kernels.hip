@@ -378,48 +378,19 @@ __device__ __forceinline__ uint32_t nvfp4_codes8(const uint4 a, float eff, float
 // Tiles: 512-column segment x 32 rows (4 waves x 8 rows).  Lane pair
 // (2k, 2k+1) holds one 16-element block, 8 elements each, so every load and
 // store instruction of a wave is contiguous; the block amax is one DPP swap.
-__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
-                                                          int64_t rows, int64_t cols,
-                                                          uint8_t *__restrict__ q,
-                                                          uint8_t *__restrict__ s_out,
-                                                          float *__restrict__ g_out,
-                                                          const uint32_t *__restrict__ partial,
-                                                          int npartial, int64_t nseg)
+// The per-block steps for one wave's 8 rows of a tile (rows r0 + 4i), given
+// the global scale g (NaN when the tensor or scale group holds NaN/Inf).
+__device__ __forceinline__ void nvfp4_encode_rows(const uint4 (&v)[kRowsNv / 4], int64_t r0,
+                                                  int64_t rows, int64_t cols, int64_t col,
+                                                  uint8_t *__restrict__ q,
+                                                  uint8_t *__restrict__ s_out, float g,
+                                                  bool nonfinite)
 {
-    __shared__ uint32_t red[4];
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg;
-    const int64_t rb = tile / nseg;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-    const int64_t col = seg * kSegNv + lane * 8;
     const bool cin = col < cols;  // cols % 16 == 0: a block (lane pair) is all in or all out
-    constexpr int kR = kRowsNv / 4;  // rows per wave
-
-    // issue this wave's loads first, then reduce the amax partials meanwhile
-    uint4 v[kR];
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-        const int64_t r = rb * kRowsNv + wave + 4 * i;
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (cin && r < rows) v[i] = ld16<kNTLoadNvQuant>(x + r * cols + col);
-    }
-    uint32_t am = 0;
-    for (int k = threadIdx.x; k < npartial; k += 256) am = max(am, partial[k]);
-    am = wave_max(am);
-    if (lane == 0) red[wave] = am;
-    __syncthreads();
-    am = max(max(red[0], red[1]), max(red[2], red[3]));
-
-    const bool nonfinite = am >= 0x7F80u;
-    const float A = __uint_as_float(am << 16);
-    const float g = A / 2688.0f;                 // 2688 = 448 * 6
     const float d = 6.0f * g;
-    if (tile == 0 && threadIdx.x == 0) *g_out = nonfinite ? __builtin_nanf("") : g;
-
 #pragma unroll
-    for (int i = 0; i < kR; ++i) {
-        const int64_t r = rb * kRowsNv + wave + 4 * i;
+    for (int i = 0; i < kRowsNv / 4; ++i) {
+        const int64_t r = r0 + 4 * i;
         const bool ok = cin && r < rows;
         const uint32_t h = amax8(v[i]);
         const uint32_t b = max(h, dpp_swap1(h));  // the block's amax (lane pair)
@@ -444,6 +415,126 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
             s_out[r * (cols >> 4) + (col >> 4)] = (uint8_t)s;
         }
     }
+}
+
+// This wave's 8 rows of a tile (16 bytes of x per lane and row).
+template <bool kNT>
+__device__ __forceinline__ void nvfp4_load_rows(const uint16_t *__restrict__ x, int64_t r0,
+                                                int64_t rows, int64_t cols, int64_t col,
+                                                uint4 (&v)[kRowsNv / 4])
+{
+#pragma unroll
+    for (int i = 0; i < kRowsNv / 4; ++i) {
+        const int64_t r = r0 + 4 * i;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (col < cols && r < rows) v[i] = ld16<kNT>(x + r * cols + col);
+    }
+}
+
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t rows, int64_t cols,
+                                                          uint8_t *__restrict__ q,
+                                                          uint8_t *__restrict__ s_out,
+                                                          float *__restrict__ g_out,
+                                                          const uint32_t *__restrict__ partial,
+                                                          int npartial, int64_t nseg)
+{
+    __shared__ uint32_t red[4];
+    const int64_t tile = blockIdx.x;
+    const int64_t seg = tile % nseg;
+    const int64_t rb = tile / nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int64_t col = seg * kSegNv + lane * 8;
+    const int64_t r0 = rb * kRowsNv + wave;
+
+    // issue this wave's loads first, then reduce the amax partials meanwhile
+    uint4 v[kRowsNv / 4];
+    nvfp4_load_rows<kNTLoadNvQuant>(x, r0, rows, cols, col, v);
+    uint32_t am = 0;
+    for (int k = threadIdx.x; k < npartial; k += 256) am = max(am, partial[k]);
+    am = wave_max(am);
+    if (lane == 0) red[wave] = am;
+    __syncthreads();
+    am = max(max(red[0], red[1]), max(red[2], red[3]));
+
+    const bool nonfinite = am >= 0x7F80u;
+    const float A = __uint_as_float(am << 16);
+    const float g = nonfinite ? __builtin_nanf("") : A / 2688.0f;  // 2688 = 448 * 6
+    if (tile == 0 && threadIdx.x == 0) *g_out = g;
+    nvfp4_encode_rows(v, r0, rows, cols, col, q, s_out, g, nonfinite);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped NVFP4: many tensors, the global scale shared within caller-given
+// scale groups (a fused gated-MoE gate_up weight uses one group per half for
+// QAT, or one group for both halves to export a shared weight_scale_2).  Three
+// launches over the flattened (tensor, tile) space of 512-column x 32-row
+// tiles: per-tile amax partials; one workgroup per scale group reducing its
+// members' partials to g; per-tile encoding with the tensor's group scale.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nvfp4_g_amax_kernel(const NvEntry *__restrict__ table,
+                                                           const int32_t *__restrict__ starts,
+                                                           int32_t n, uint32_t *__restrict__ partial)
+{
+    __shared__ uint32_t red[4];
+    const int32_t t = (int32_t)blockIdx.x;
+    const NvEntry E = table[find_entry(starts, n, t)];
+    const int32_t local = t - E.tile_begin;
+    const int64_t seg = local % E.nseg, rb = local / E.nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    uint4 v[kRowsNv / 4];
+    nvfp4_load_rows<kNTLoadNvAmax>(E.x, rb * kRowsNv + wave, E.rows, E.cols, seg * kSegNv + lane * 8,
+                                   v);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kRowsNv / 4; ++i) m = max(m, amax8(v[i]));
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[t] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void nvfp4_g_reduce_kernel(const int32_t *__restrict__ starts,
+                                                             const int32_t *__restrict__ groups,
+                                                             int32_t n, int32_t total_tiles,
+                                                             const uint32_t *__restrict__ partial,
+                                                             float *__restrict__ gs)
+{
+    __shared__ uint32_t red[4];
+    const int32_t j = (int32_t)blockIdx.x;
+    uint32_t m = 0;
+    for (int32_t i = 0; i < n; ++i) {  // uniform loop over the entries
+        if (groups[i] != j) continue;
+        const int32_t t1 = i + 1 < n ? starts[i + 1] : total_tiles;
+        for (int32_t k = starts[i] + (int32_t)threadIdx.x; k < t1; k += 256) m = max(m, partial[k]);
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = max(max(red[0], red[1]), max(red[2], red[3]));
+        const bool nonfinite = m >= 0x7F80u;
+        gs[j] = nonfinite ? __builtin_nanf("") : __uint_as_float(m << 16) / 2688.0f;
+    }
+}
+
+__global__ __launch_bounds__(256) void nvfp4_g_quant_kernel(const NvEntry *__restrict__ table,
+                                                            const int32_t *__restrict__ starts,
+                                                            int32_t n, const float *__restrict__ gs)
+{
+    const int32_t t = (int32_t)blockIdx.x;
+    const NvEntry E = table[find_entry(starts, n, t)];
+    const int32_t local = t - E.tile_begin;
+    const int64_t seg = local % E.nseg, rb = local / E.nseg;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t col = seg * kSegNv + lane * 8, r0 = rb * kRowsNv + wave;
+    uint4 v[kRowsNv / 4];
+    nvfp4_load_rows<kNTLoadNvQuant>(E.x, r0, E.rows, E.cols, col, v);
+    const float g = gs[E.group];
+    nvfp4_encode_rows(v, r0, E.rows, E.cols, col, E.q, E.s, g, g != g);
 }
 
 // 8 packed E2M1 nibbles (one word) -> 8 bf16, effective scale eff.
@@ -599,6 +690,34 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,
                        cols, q, s, g, ws, ablocks, nseg);
+    return hipGetLastError();
+}
+
+int64_t nvfp4_tiles(int64_t rows, int64_t cols, int64_t *nseg)
+{
+    const int64_t ns = (cols + kSegNv - 1) / kSegNv;
+    if (nseg) *nseg = ns;
+    return ns * ((rows + kRowsNv - 1) / kRowsNv);
+}
+
+hipError_t launch_nvfp4_grouped(const NvEntry *table, const int32_t *starts, const int32_t *groups,
+                                int32_t n, uint32_t *partial, int64_t total_tiles, float *gs,
+                                int32_t n_groups, hipStream_t stream)
+{
+    if (n <= 0 && n_groups <= 0) return hipSuccess;
+    if (total_tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (total_tiles > 0) {
+        hipLaunchKernelGGL(nvfp4_g_amax_kernel, dim3((unsigned)total_tiles), dim3(256), 0, stream,
+                           table, starts, n, partial);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(nvfp4_g_reduce_kernel, dim3((unsigned)n_groups), dim3(256), 0, stream,
+                       starts, groups, n, (int32_t)total_tiles, partial, gs);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || total_tiles == 0) return err;
+    hipLaunchKernelGGL(nvfp4_g_quant_kernel, dim3((unsigned)total_tiles), dim3(256), 0, stream,
+                       table, starts, n, gs);
     return hipGetLastError();
 }
 

@@ -61,6 +61,24 @@ constexpr int kNvAmaxBlocks = 1024;
 
 hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
                               uint8_t *s, float *g, uint32_t *ws, hipStream_t stream);
+// Launch table entry of grouped NVFP4 (staged in the caller's workspace,
+// followed by int32 arrays of first tiles and scale groups, then one uint32
+// amax partial per tile).  Tiles: 512 columns x 32 rows.
+struct NvEntry {
+    const uint16_t *x;
+    uint8_t *q;
+    uint8_t *s;
+    int64_t rows, cols;
+    int64_t nseg;
+    int32_t tile_begin;
+    int32_t group;
+};
+
+hipError_t launch_nvfp4_grouped(const NvEntry *table, const int32_t *starts, const int32_t *groups,
+                                int32_t n, uint32_t *partial, int64_t total_tiles, float *gs,
+                                int32_t n_groups, hipStream_t stream);
+int64_t nvfp4_tiles(int64_t rows, int64_t cols, int64_t *nseg);
+
 hipError_t launch_nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float *g,
                                 int64_t rows, int64_t cols, uint16_t *out, hipStream_t stream);
 

@@ -487,21 +487,7 @@ __global__ __launch_bounds__(256) void mx_grouped_kernel(const GroupEntry *__res
                                                          int32_t n)
 {
     const int32_t t = (int32_t)blockIdx.x;
-    // 64-way search for the last entry whose first tile is <= t: each round,
-    // lane k samples starts[lo + k*step]; the sampled values increase with k,
-    // so the lanes that pass form a prefix and the highest one narrows the
-    // range to one step.  384 tensors take two dependent reads instead of nine.
-    const int lane = threadIdx.x & (kWave - 1);
-    int lo = 0, m = n;  // invariant: starts[lo] <= t, and the answer is in [lo, lo + m)
-    while (m > 1) {
-        const int step = (m + kWave - 1) / kWave;
-        const int off = lane * step;
-        const bool le = off < m && starts[lo + off] <= t;
-        const int last = 63 - __builtin_clzll(__ballot(le));  // lane 0 always passes
-        lo += last * step;
-        m = min(step, m - last * step);
-    }
-    lo = __builtin_amdgcn_readfirstlane(lo);
+    const int lo = find_entry(starts, n, t);
     const GroupEntry E = table[lo];
     const int32_t local = t - starts[lo];
     const int32_t nseg = (int32_t)E.nseg;

@@ -335,6 +335,84 @@ mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t
                                             static_cast<uint32_t *>(workspace), as_stream(stream)));
 }
 
+namespace {
+size_t round16(size_t v) { return (v + 15) / 16 * 16; }
+size_t nv_table_bytes(int32_t n)
+{
+    return round16((size_t)n * (sizeof(mxq::NvEntry) + 2 * sizeof(int32_t)));
+}
+}  // namespace
+
+size_t nvfp4_grouped_workspace_size(const nvfp4_group_desc *descs, int32_t n)
+{
+    if (n <= 0 || !descs) return 0;
+    size_t tiles = 0;
+    for (int32_t i = 0; i < n; ++i)
+        if (descs[i].rows > 0 && descs[i].cols > 0)
+            tiles += (size_t)mxq::nvfp4_tiles(descs[i].rows, descs[i].cols, nullptr);
+    return nv_table_bytes(n) + round16(tiles * sizeof(uint32_t));
+}
+
+mxq_status nvfp4_quantize_grouped(const nvfp4_group_desc *descs, int32_t n, float *global_scales,
+                                  int32_t n_groups, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    if (n < 0 || n_groups < 0) return MXQ_EINVAL;
+    if (n > 0 && (!descs || n_groups == 0)) return MXQ_EINVAL;
+    if (n_groups == 0) return MXQ_OK;
+    if (!global_scales) return MXQ_EINVAL;
+    if (!aligned(global_scales, 4)) return MXQ_EALIGN;
+    std::vector<mxq::NvEntry> table;
+    std::vector<int32_t> starts, groups;
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const nvfp4_group_desc &d = descs[i];
+        if (d.rows < 0 || d.cols < 0 || d.scale_group < 0 || d.scale_group >= n_groups)
+            return MXQ_EINVAL;
+        if (d.cols % 16 != 0) return MXQ_ESHAPE;
+        if (d.rows == 0 || d.cols == 0) continue;
+        if (!d.x || !d.q || !d.s) return MXQ_EINVAL;
+        if (!aligned(d.x, 16) || !aligned(d.q, 4)) return MXQ_EALIGN;
+        if (!fits(d.rows, d.cols)) return MXQ_ESIZE;
+        mxq::NvEntry e;
+        e.x = d.x;
+        e.q = d.q;
+        e.s = d.s;
+        e.rows = d.rows;
+        e.cols = d.cols;
+        const int64_t t = mxq::nvfp4_tiles(d.rows, d.cols, &e.nseg);
+        e.tile_begin = (int32_t)tiles;
+        e.group = d.scale_group;
+        if (__builtin_add_overflow(tiles, t, &tiles) || tiles > 0x7FFFFFFF) return MXQ_ESIZE;
+        table.push_back(e);
+        starts.push_back(e.tile_begin);
+        groups.push_back(e.group);
+    }
+    if (!workspace) return MXQ_EINVAL;
+    if (!aligned(workspace, 16)) return MXQ_EALIGN;
+    if (workspace_bytes < nvfp4_grouped_workspace_size(descs, n)) return MXQ_ESIZE;
+    // workspace: [entries x n][first tiles x n][groups x n] | partials
+    const size_t m = table.size();
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const size_t tbytes = (size_t)n * sizeof(mxq::NvEntry);
+    std::vector<unsigned char> stage(tbytes + 2 * (size_t)n * sizeof(int32_t), 0);
+    if (m) {
+        memcpy(stage.data(), table.data(), m * sizeof(mxq::NvEntry));
+        memcpy(stage.data() + tbytes, starts.data(), m * sizeof(int32_t));
+        memcpy(stage.data() + tbytes + (size_t)n * sizeof(int32_t), groups.data(),
+               m * sizeof(int32_t));
+        // pageable source: the copy has consumed it by the time it returns
+        if (hipMemcpyAsync(ws, stage.data(), stage.size(), hipMemcpyHostToDevice,
+                           as_stream(stream)) != hipSuccess)
+            return MXQ_EHIP;
+    }
+    return from_hip(mxq::launch_nvfp4_grouped(
+        reinterpret_cast<const mxq::NvEntry *>(ws), reinterpret_cast<const int32_t *>(ws + tbytes),
+        reinterpret_cast<const int32_t *>(ws + tbytes + (size_t)n * sizeof(int32_t)), (int32_t)m,
+        reinterpret_cast<uint32_t *>(ws + nv_table_bytes(n)), tiles, global_scales, n_groups,
+        as_stream(stream)));
+}
+
 mxq_status nvfp4_dequantize(const uint8_t *q_packed, const uint8_t *s_e4m3,
                             const float *global_scale, int64_t rows, int64_t cols, uint16_t *out,
                             void *stream)

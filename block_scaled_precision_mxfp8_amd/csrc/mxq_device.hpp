@@ -66,6 +66,27 @@ __device__ __forceinline__ uint32_t dpp_swap2(uint32_t v)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
 }
 
+// Index of the last entry whose first tile is <= t, for strictly increasing
+// starts[0..n) with starts[0] == 0 (grouped launches).  64-way search: each
+// round, lane k samples starts[lo + k*step]; the sampled values increase with
+// k, so the lanes that pass form a prefix and the highest one narrows the
+// range to one step.  384 entries take two dependent reads instead of nine.
+// The result is wave-uniform.
+__device__ __forceinline__ int find_entry(const int32_t *__restrict__ starts, int n, int32_t t)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    int lo = 0, m = n;  // invariant: starts[lo] <= t, and the answer is in [lo, lo + m)
+    while (m > 1) {
+        const int step = (m + kWave - 1) / kWave;
+        const int off = lane * step;
+        const bool le = off < m && starts[lo + off] <= t;
+        const int last = 63 - __builtin_clzll(__ballot(le));  // lane 0 always passes
+        lo += last * step;
+        m = min(step, m - last * step);
+    }
+    return __builtin_amdgcn_readfirstlane(lo);
+}
+
 // Max over the 4 lanes of a quad (one 32-element row group = 4 lanes x 8).
 __device__ __forceinline__ uint32_t quad_max(uint32_t v)
 {

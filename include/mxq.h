@@ -288,6 +288,41 @@ mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t
                           uint8_t *s_e4m3, float *global_scale, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * Grouped NVFP4 with global scales shared within scale groups (xorl PR #30,
+ * deep review item 3: a fused gated-MoE gate_up weight is quantized with one
+ * global scale per half for QAT, and with one weight_scale_2 shared by gate
+ * and up for the fused serving kernel).  Tensor i belongs to scale group
+ * descs[i].scale_group in [0, n_groups); a group's A is the max |x| over all
+ * its tensors (NaN/Inf in any makes the group all-NaN as in nvfp4_quantize),
+ * global_scales[group] = fl32(A / 2688), and every member is quantized with
+ * that scale exactly as nvfp4_quantize does.  A group without members gets
+ * 0.  One call; tensors with rows == 0 or cols == 0 are skipped.
+ *   descs          host array of n descriptors: x [rows, cols] bf16
+ *                  contiguous 16-byte aligned, q [rows, cols/2] 4-byte
+ *                  aligned, s [rows, cols/16]; cols % 16 == 0
+ *   global_scales  device float[n_groups], 4-byte aligned
+ *   workspace      >= nvfp4_grouped_workspace_size(descs, n) bytes of device
+ *                  memory, 16-byte aligned, caller-owned: the launch table and
+ *                  one amax partial per 512 x 32 tile (no initial contents
+ *                  needed; calls that overlap on one workspace race).  It is
+ *                  filled by an asynchronous copy on `stream`.
+ */
+typedef struct nvfp4_group_desc {
+    const uint16_t *x;
+    uint8_t *q;
+    uint8_t *s;
+    int64_t rows, cols;
+    int32_t scale_group;
+    int32_t reserved; /* set to 0 */
+} nvfp4_group_desc;
+
+size_t nvfp4_grouped_workspace_size(const nvfp4_group_desc *descs, int32_t n);
+
+mxq_status nvfp4_quantize_grouped(const nvfp4_group_desc *descs, int32_t n, float *global_scales,
+                                  int32_t n_groups, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* NVFP4 dequantization: out = bf16_RNE(fl32(E2M1(q) * eff)),
  * eff = fl32(E4M3(s) * g); a NaN product gives the quiet NaN with the
  * nibble's sign.  Shapes as nvfp4_quantize; out 16-byte aligned. */

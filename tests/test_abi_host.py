@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                  "mxq_grouped_workspace_size", "nvfp4_workspace_size", "mxfp4_quantize",
                  "mxfp4_dequantize", "mxfp4_fake_quant", "mxq_quantize_colwise_t",
                  "blockfp8_to_mxfp8", "blockfp8_quantize_1x128", "blockfp8_dequantize_1x128",
-                 "blockfp8_fake_quant_1x128"]:
+                 "blockfp8_fake_quant_1x128", "nvfp4_quantize_grouped",
+                 "nvfp4_grouped_workspace_size"]:
         assert want in names
     assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
 
@@ -206,6 +207,34 @@ def test_blockfp8_1x128_errors(lib):
     assert fq(P16, 4, 32, NULL, NULL) == mxq.MXQ_EINVAL
     assert fq(P2, 4, 32, P16, NULL) == mxq.MXQ_EALIGN
     assert fq(P16, 4, 12, P16, NULL) == mxq.MXQ_ESHAPE
+
+
+def test_nvfp4_grouped_errors(lib):
+    f = lib.nvfp4_quantize_grouped
+    descs = (mxq.NvGroupDesc * 2)()
+    descs[0] = mxq.NvGroupDesc(0x10000, 0x20000, 0x30000, 8, 64, 0, 0)
+    descs[1] = mxq.NvGroupDesc(0x40000, 0x50000, 0x60000, 40, 32, 1, 0)
+    ws = lib.nvfp4_grouped_workspace_size(descs, 2)
+    assert ws >= 2 * 16 and ws % 16 == 0
+    assert lib.nvfp4_grouped_workspace_size(descs, 0) == 0
+    assert f(descs, -1, P16, 2, P16, ws, NULL) == mxq.MXQ_EINVAL
+    assert f(descs, 2, P16, 0, P16, ws, NULL) == mxq.MXQ_EINVAL            # no groups
+    assert f(NULL, 2, P16, 2, P16, ws, NULL) == mxq.MXQ_EINVAL
+    assert f(descs, 2, NULL, 2, P16, ws, NULL) == mxq.MXQ_EINVAL           # no global scales
+    assert f(descs, 2, P2, 2, P16, ws, NULL) == mxq.MXQ_EALIGN             # gs 4-aligned
+    assert f(descs, 2, P16, 1, P16, ws, NULL) == mxq.MXQ_EINVAL            # group 1 out of range
+    assert f(descs, 2, P16, 2, NULL, ws, NULL) == mxq.MXQ_EINVAL           # no workspace
+    assert f(descs, 2, P16, 2, P8, ws, NULL) == mxq.MXQ_EALIGN             # workspace 16-aligned
+    assert f(descs, 2, P16, 2, P16, ws - 1, NULL) == mxq.MXQ_ESIZE
+    descs[1] = mxq.NvGroupDesc(0x40000, 0x50000, 0x60000, 40, 24, 1, 0)   # cols % 16
+    assert f(descs, 2, P16, 2, P16, ws, NULL) == mxq.MXQ_ESHAPE
+    descs[1] = mxq.NvGroupDesc(0x40008, 0x50000, 0x60000, 40, 32, 1, 0)   # x 16-aligned
+    assert f(descs, 2, P16, 2, P16, ws, NULL) == mxq.MXQ_EALIGN
+    descs[1] = mxq.NvGroupDesc(0x40000, 0x50002, 0x60000, 40, 32, 1, 0)   # q 4-aligned
+    assert f(descs, 2, P16, 2, P16, ws, NULL) == mxq.MXQ_EALIGN
+    descs[1] = mxq.NvGroupDesc(0x40000, 0, 0x60000, 40, 32, 1, 0)         # NULL q
+    assert f(descs, 2, P16, 2, P16, ws, NULL) == mxq.MXQ_EINVAL
+    assert f(descs, 0, P16, 0, NULL, 0, NULL) == mxq.MXQ_OK
 
 
 def test_mxfp4_errors(lib):
