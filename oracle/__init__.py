@@ -102,6 +102,12 @@ class Oracle:
         L.orc_blockfp8_dequantize_rect.restype = None
         L.orc_blockfp8_fake_quant_1x128.argtypes = [_u16p, _i64, _i64, _u16p]
         L.orc_blockfp8_fake_quant_1x128.restype = ctypes.c_int
+        L.orc_blockfp8_quantize_gkn.argtypes = [_u16p, _i64, _i64, _i64, ctypes.c_int32, _u8p,
+                                                _f32p]
+        L.orc_blockfp8_quantize_gkn.restype = None
+        L.orc_blockfp8_dequantize_gkn.argtypes = [_u8p, _f32p, _i64, _i64, _i64, ctypes.c_int32,
+                                                  _u16p]
+        L.orc_blockfp8_dequantize_gkn.restype = None
         L.orc_blockfp8_quantize.argtypes = [_u16p, _i64, _i64, ctypes.c_int32, _u8p, _f32p]
         L.orc_blockfp8_quantize.restype = None
         L.orc_blockfp8_dequantize.argtypes = [_u8p, _f32p, _i64, _i64, ctypes.c_int32, _u16p]
@@ -250,6 +256,26 @@ class Oracle:
         out = np.empty((rows, cols), np.uint16)
         self.L.orc_blockfp8_dequantize(_p(q, _u8p), _p(S, _f32p), rows, cols, int(blk),
                                        _p(out, _u16p))
+        return out
+
+    def blockfp8_quantize_gkn(self, x: np.ndarray, blk: int = 128):
+        """x: uint16 [G, K, N] -> (q [G, K, N] u8, S [G, ceil(K/blk), ceil(N/blk)] f32)."""
+        x = np.ascontiguousarray(x)
+        assert x.dtype == np.uint16 and x.ndim == 3
+        G, K, N = x.shape
+        q = np.empty((G, K, N), np.uint8)
+        S = np.empty((G, (K + blk - 1) // blk, (N + blk - 1) // blk), np.float32)
+        self.L.orc_blockfp8_quantize_gkn(_p(x, _u16p), G, K, N, int(blk), _p(q, _u8p),
+                                         _p(S, _f32p))
+        return q, S
+
+    def blockfp8_dequantize_gkn(self, q: np.ndarray, S: np.ndarray, blk: int = 128):
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        S = np.ascontiguousarray(S, dtype=np.float32)
+        G, K, N = q.shape
+        out = np.empty((G, K, N), np.uint16)
+        self.L.orc_blockfp8_dequantize_gkn(_p(q, _u8p), _p(S, _f32p), G, K, N, int(blk),
+                                           _p(out, _u16p))
         return out
 
     def blockfp8_quantize_rect(self, x: np.ndarray, br: int, bc: int):

@@ -503,6 +503,26 @@ void orc_blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows,
     orc_blockfp8_dequantize_rect(q, scale, rows, cols, blk, blk, out);
 }
 
+/* Block-FP8 of a stack of G matrices [G, K, N] (grouped GEMM weights, the
+ * `_gkn` variant [xorl, "What looked solid"]): every slice [K, N] is
+ * quantized on its own with blk x blk tiles, so no tile crosses slices;
+ * scale is [G, ceil(K/blk), ceil(N/blk)]. */
+void orc_blockfp8_quantize_gkn(const uint16_t *x, int64_t G, int64_t K, int64_t N, int32_t blk,
+                               uint8_t *q, float *scale)
+{
+    int64_t ts = ((K + blk - 1) / blk) * ((N + blk - 1) / blk);
+    for (int64_t g = 0; g < G; ++g)
+        orc_blockfp8_quantize(x + g * K * N, K, N, blk, q + g * K * N, scale + g * ts);
+}
+
+void orc_blockfp8_dequantize_gkn(const uint8_t *q, const float *scale, int64_t G, int64_t K,
+                                 int64_t N, int32_t blk, uint16_t *out)
+{
+    int64_t ts = ((K + blk - 1) / blk) * ((N + blk - 1) / blk);
+    for (int64_t g = 0; g < G; ++g)
+        orc_blockfp8_dequantize(q + g * K * N, scale + g * ts, K, N, blk, out + g * K * N);
+}
+
 /* 1 x 128 blocks along each row: the activation recipe, and with
  * dequantization right after it the fake quantization fp8_simulate_qat(x,
  * 128) ["V4 mxfp4" (miles PR #1372), compressor review; fp32 scale storage per

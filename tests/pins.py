@@ -681,3 +681,19 @@ def pin_nvfp4_grouped(orc, xs, groups, n_groups):
             rq, rs, rg = orc.nvfp4_quantize(np.concatenate([x, extra]))
             assert rg.view(np.uint32)[0] == gs[j].view(np.uint32)
             assert np.array_equal(q, rq[:-1]) and np.array_equal(s, rs[:-1])
+
+
+def pin_blockfp8_gkn(orc, x3):
+    """[G, K, N] block-FP8: every slice equals the torch composition of
+    128 x 128 block-FP8 on that slice alone (no tile crosses a slice), and
+    dequantization per slice matches torch's products."""
+    q, S = orc.blockfp8_quantize_gkn(x3)
+    dq = orc.blockfp8_dequantize_gkn(q, S)
+    for g in range(x3.shape[0]):
+        rq, rS = torch_blockfp8(np.ascontiguousarray(x3[g]), 128)
+        assert np.array_equal(S[g].view(np.uint32), rS.view(np.uint32))
+        assert np.array_equal(q[g], rq)
+        K, N = x3.shape[1:]
+        Sx = np.repeat(np.repeat(S[g], 128, 0), 128, 1)[:K, :N]
+        v = torch.from_numpy(q[g].copy()).view(torch.float8_e4m3fn).float() * torch.from_numpy(Sx)
+        assert np.array_equal(dq[g], v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))

@@ -41,6 +41,8 @@ MUTANTS = [
     ("nvfp4 group amax over the first member only",
      "for (int32_t i = 0; i < n; ++i) nv_amax(xs[i], rows[i] * cols[i], &A[group[i]], &nf[group[i]]);",
      "for (int32_t i = 0; i < n; ++i) if (A[group[i]] == 0.0) nv_amax(xs[i], rows[i] * cols[i], &A[group[i]], &nf[group[i]]);"),
+    ("gkn tiles cross slices", "orc_blockfp8_quantize(x + g * K * N, K, N, blk, q + g * K * N, scale + g * ts);",
+     "orc_blockfp8_quantize(x + g * K * N, K, N, blk, q + g * K * N, scale + g * ts);\n    if (G > 1 && K % blk) orc_blockfp8_quantize(x, G * K, N, blk, q, scale);"),
     ("colwise group stride", "q[(r0 + i) * cols + c] = mx_encode(g[i], s);",
      "q[(r0 + i) * cols + c] = mx_encode(g[i], (uint8_t)(s + (i == 31)));"),
     ("blockfp8 divisor 447", "S = (float)amax / 448.0f;", "S = (float)amax / 447.0f;"),
@@ -95,6 +97,7 @@ def all_pins(orc):
     pins.pin_blockfp8(orc, z, 128)
     pins.pin_nvfp4(orc, workloads.random_bf16((64, 256), 21))
     pins.pin_requant_pow2_tiles(orc)
+    pins.pin_blockfp8_gkn(orc, workloads.random_bf16((3 * 200, 136), 900).reshape(3, 200, 136))
     hx = [workloads.random_bf16((32, 64), 600 + i, std=0.02 * (1 + i)) for i in range(4)]
     pins.pin_nvfp4_grouped(orc, hx, [0, 0, 1, 1], 3)
     y = workloads.random_bf16((33, 200), 533)

@@ -233,3 +233,10 @@ def test_nvfp4_grouped_nonfinite_member(orc):
     outs, gs = orc.nvfp4_quantize_grouped(xs, [i // 2 for i in range(len(xs))], 3)
     assert np.isnan(gs[1]) and np.isfinite(gs[0]) and np.isfinite(gs[2])
     assert np.all(outs[2][1] == 0x7F) and np.all(outs[3][1] == 0x7F)
+
+
+@pytest.mark.parametrize("shape", [(3, 200, 136), (2, 128, 256), (4, 33, 8)])
+def test_blockfp8_gkn(orc, shape):
+    x = workloads.random_bf16((shape[0] * shape[1], shape[2]), 700 + shape[1]).reshape(shape)
+    x[0, :min(shape[1], 128), :min(shape[2], 128)] = 0
+    pins.pin_blockfp8_gkn(orc, x)
