@@ -52,6 +52,8 @@ SIGNATURES = {
     "mxq_quantize_rowwise_grouped": (ctypes.c_int, [_vp, _i32, _vp, _sz, _vp]),
     "blockfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
     "blockfp8_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i32, _vp, _vp]),
+    "blockfp8_quantize_gkn": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "blockfp8_dequantize_gkn": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp]),
     "blockfp8_quantize_1x128": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "blockfp8_dequantize_1x128": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "blockfp8_fake_quant_1x128": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
@@ -343,6 +345,32 @@ def mxfp4_simulate_qat(x: torch.Tensor) -> torch.Tensor:
     st = load().mxfp4_fake_quant(_ptr(x2), rows, cols, _ptr(out), _stream(x2))
     _check("mxfp4_fake_quant", st)
     return out.view(x.shape)
+
+
+def blockfp8_quantize_gkn(x: torch.Tensor, blk: int = 128):
+    """Block-FP8 of a [G, K, N] bf16 stack, 128 x 128 tiles per slice: (q uint8
+    [G, K, N], S float32 [G, ceil(K/128), ceil(N/128)])."""
+    _need_bf16_cuda(x)
+    if x.dim() != 3:
+        raise ValueError("blockfp8_quantize_gkn expects a [G, K, N] tensor")
+    x = x.contiguous()
+    G, K, N = x.shape
+    q = torch.empty((G, K, N), dtype=torch.uint8, device=x.device)
+    S = torch.empty((G, -(-K // blk), -(-N // blk)), dtype=torch.float32, device=x.device)
+    st = load().blockfp8_quantize_gkn(_ptr(x), G, K, N, blk, _ptr(q), _ptr(S), _stream(x))
+    _check("blockfp8_quantize_gkn", st)
+    return q, S
+
+
+def blockfp8_dequantize_gkn(q: torch.Tensor, S: torch.Tensor, blk: int = 128) -> torch.Tensor:
+    q = q.contiguous()
+    S = S.contiguous()
+    G, K, N = q.shape
+    out = torch.empty((G, K, N), dtype=torch.bfloat16, device=q.device)
+    st = load().blockfp8_dequantize_gkn(_ptr(q.view(torch.uint8)), _ptr(S), G, K, N, blk,
+                                        _ptr(out), _stream(q))
+    _check("blockfp8_dequantize_gkn", st)
+    return out
 
 
 def blockfp8_quantize_1x128(x: torch.Tensor, fake_quant: bool = False):

@@ -61,14 +61,21 @@ __device__ __forceinline__ uint2 bfp8_encode8(uint4 v, float div, float y, bool 
 // ---------------------------------------------------------------------------
 // Block-FP8: one workgroup per 128 x 128 tile.  Thread t loads 8 rows
 // (t/16 + 16k) x 8 columns ((t%16)*8): each wave load covers 4 rows x 256 B.
+// A stack of slices [G, rows, cols] (ts tiles each) is quantized slice by
+// slice: no tile crosses a slice boundary.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restrict__ x,
                                                          int64_t rows, int64_t cols,
                                                          uint8_t *__restrict__ q,
-                                                         float *__restrict__ scale, int64_t tc)
+                                                         float *__restrict__ scale, int64_t tc,
+                                                         int64_t ts)
 {
     __shared__ uint32_t red[4];
-    const int64_t bi = blockIdx.x / tc, bj = blockIdx.x % tc;
+    const int64_t slice = blockIdx.x / ts, t = blockIdx.x % ts;
+    x += slice * rows * cols;
+    q += slice * rows * cols;
+    scale += slice * ts;
+    const int64_t bi = t / tc, bj = t % tc;
     const int tid = threadIdx.x;
     const int64_t col = bj * kBlk + (tid & 15) * 8;
     const int64_t rbase = bi * kBlk + (tid >> 4);
@@ -158,9 +165,16 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
                                                            const float *__restrict__ scale,
                                                            int64_t rows, int64_t cols,
                                                            uint16_t *__restrict__ out, int64_t tc,
-                                                           int64_t nseg)
+                                                           int64_t nseg, int64_t slice_tiles,
+                                                           int64_t slice_scales)
 {
-    const int64_t tile = blockIdx.x;
+    // slices [G, rows, cols] of 128 x 128 tiles: slice_tiles launch tiles and
+    // slice_scales scales each (one slice when slice_tiles is the grid size)
+    const int64_t slice = blockIdx.x / slice_tiles;
+    q += slice * rows * cols;
+    out += slice * rows * cols;
+    scale += slice * slice_scales;
+    const int64_t tile = blockIdx.x % slice_tiles;
     const int64_t seg = tile % nseg;
     const int64_t rb = tile / nseg;
     const int lane = threadIdx.x & (kWave - 1);
@@ -613,31 +627,35 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__res
 // Host launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
-                             float *scale, hipStream_t stream)
+hipError_t launch_bfp8_quant(const uint16_t *x, int64_t slices, int64_t rows, int64_t cols,
+                             uint8_t *q, float *scale, hipStream_t stream)
 {
     const int64_t tr = (rows + kBlk - 1) / kBlk, tc = (cols + kBlk - 1) / kBlk;
-    if (tr * tc <= 0) return hipSuccess;
-    if (tr * tc > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bfp8_quant_kernel, dim3((unsigned)(tr * tc)), dim3(256), 0, stream, x, rows,
-                       cols, q, scale, tc);
+    const int64_t ts = tr * tc;
+    if (ts <= 0 || slices <= 0) return hipSuccess;
+    if (ts > 0x7FFFFFFF / slices) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bfp8_quant_kernel, dim3((unsigned)(ts * slices)), dim3(256), 0, stream, x,
+                       rows, cols, q, scale, tc, ts);
     return hipGetLastError();
 }
 
-hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
-                               bool row_scales, uint16_t *out, hipStream_t stream)
+hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t slices,
+                               int64_t rows, int64_t cols, bool row_scales, uint16_t *out,
+                               hipStream_t stream)
 {
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
-    if (tiles <= 0) return hipSuccess;
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const int64_t per = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    if (per <= 0 || slices <= 0) return hipSuccess;
+    if (per > 0x7FFFFFFF / slices) return hipErrorInvalidConfiguration;
+    const int64_t tiles = per * slices;
     const int64_t tc = (cols + kBlk - 1) / kBlk;
+    const int64_t scales = (row_scales ? rows : (rows + kBlk - 1) / kBlk) * tc;
     if (row_scales)
         hipLaunchKernelGGL((bfp8_dequant_kernel<true>), dim3((unsigned)tiles), dim3(256), 0,
-                           stream, q, scale, rows, cols, out, tc, nseg);
+                           stream, q, scale, rows, cols, out, tc, nseg, per, scales);
     else
         hipLaunchKernelGGL((bfp8_dequant_kernel<false>), dim3((unsigned)tiles), dim3(256), 0,
-                           stream, q, scale, rows, cols, out, tc, nseg);
+                           stream, q, scale, rows, cols, out, tc, nseg, per, scales);
     return hipGetLastError();
 }
 

@@ -45,11 +45,13 @@ hipError_t launch_mx4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8
 hipError_t launch_mx4_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
                               uint16_t *out, hipStream_t stream);
 
-hipError_t launch_bfp8_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
-                             float *scale, hipStream_t stream);
+// slices: a stack [slices, rows, cols] quantized slice by slice (1 for 2-D).
+hipError_t launch_bfp8_quant(const uint16_t *x, int64_t slices, int64_t rows, int64_t cols,
+                             uint8_t *q, float *scale, hipStream_t stream);
 // row_scales: 1 x 128 blocks (scale [rows, ceil(cols/128)]); else 128 x 128.
-hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
-                               bool row_scales, uint16_t *out, hipStream_t stream);
+hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t slices,
+                               int64_t rows, int64_t cols, bool row_scales, uint16_t *out,
+                               hipStream_t stream);
 hipError_t launch_bfp8_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
                              float *scale, uint16_t *fq, hipStream_t stream);
 

@@ -253,7 +253,7 @@ mxq_status blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int3
     if (!x || !q || !scale) return MXQ_EINVAL;
     if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4)) return MXQ_EALIGN;
     if (!fits(rows, cols)) return MXQ_ESIZE;
-    return from_hip(mxq::launch_bfp8_quant(x, rows, cols, q, scale, as_stream(stream)));
+    return from_hip(mxq::launch_bfp8_quant(x, 1, rows, cols, q, scale, as_stream(stream)));
 }
 
 mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t rows, int64_t cols,
@@ -265,7 +265,34 @@ mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t row
     if (!q || !scale || !out) return MXQ_EINVAL;
     if (!aligned(q, 8) || !aligned(out, 16) || !aligned(scale, 4)) return MXQ_EALIGN;
     if (!fits(rows, cols)) return MXQ_ESIZE;
-    return from_hip(mxq::launch_bfp8_dequant(q, scale, rows, cols, false, out, as_stream(stream)));
+    return from_hip(mxq::launch_bfp8_dequant(q, scale, 1, rows, cols, false, out,
+                                             as_stream(stream)));
+}
+
+mxq_status blockfp8_quantize_gkn(const uint16_t *x, int64_t G, int64_t K, int64_t N, int32_t blk,
+                                 uint8_t *q, float *scale, void *stream)
+{
+    if (G < 0 || K < 0 || N < 0) return MXQ_EINVAL;
+    if (blk != 128 || N % 8 != 0) return MXQ_ESHAPE;
+    if (G == 0 || K == 0 || N == 0) return MXQ_OK;
+    if (!x || !q || !scale) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(q, 8) || !aligned(scale, 4)) return MXQ_EALIGN;
+    int64_t kn;
+    if (__builtin_mul_overflow(K, N, &kn) || !fits(G, kn)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_quant(x, G, K, N, q, scale, as_stream(stream)));
+}
+
+mxq_status blockfp8_dequantize_gkn(const uint8_t *q, const float *scale, int64_t G, int64_t K,
+                                   int64_t N, int32_t blk, uint16_t *out, void *stream)
+{
+    if (G < 0 || K < 0 || N < 0) return MXQ_EINVAL;
+    if (blk != 128 || N % 8 != 0) return MXQ_ESHAPE;
+    if (G == 0 || K == 0 || N == 0) return MXQ_OK;
+    if (!q || !scale || !out) return MXQ_EINVAL;
+    if (!aligned(q, 8) || !aligned(out, 16) || !aligned(scale, 4)) return MXQ_EALIGN;
+    int64_t kn;
+    if (__builtin_mul_overflow(K, N, &kn) || !fits(G, kn)) return MXQ_ESIZE;
+    return from_hip(mxq::launch_bfp8_dequant(q, scale, G, K, N, false, out, as_stream(stream)));
 }
 
 mxq_status blockfp8_quantize_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
@@ -290,7 +317,8 @@ mxq_status blockfp8_dequantize_1x128(const uint8_t *q, const float *scale, int64
     if (!q || !scale || !out) return MXQ_EINVAL;
     if (!aligned(q, 8) || !aligned(out, 16) || !aligned(scale, 4)) return MXQ_EALIGN;
     if (!fits(rows, cols)) return MXQ_ESIZE;
-    return from_hip(mxq::launch_bfp8_dequant(q, scale, rows, cols, true, out, as_stream(stream)));
+    return from_hip(mxq::launch_bfp8_dequant(q, scale, 1, rows, cols, true, out,
+                                             as_stream(stream)));
 }
 
 mxq_status blockfp8_fake_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,

@@ -191,6 +191,24 @@ mxq_status blockfp8_dequantize(const uint8_t *q, const float *scale, int64_t row
                                int32_t blk, uint16_t *out, void *stream);
 
 /*
+ * Block-FP8 of a stack of G matrices (grouped-GEMM weights [G, K, N], the
+ * `_gkn` variant named in xorl PR #30 "What looked solid"): each slice
+ * [K, N] is quantized as blockfp8_quantize would quantize it alone, so no
+ * 128 x 128 tile crosses a slice boundary.
+ *   x      [G, K, N] bf16, contiguous, 16-byte aligned
+ *   q      [G, K, N] E4M3 codes, 8-byte aligned
+ *   scale  [G, ceil(K/128), ceil(N/128)] fp32, 4-byte aligned
+ * Shape: blk == 128; N % 8 == 0.
+ */
+mxq_status blockfp8_quantize_gkn(const uint16_t *x, int64_t G, int64_t K, int64_t N, int32_t blk,
+                                 uint8_t *q, float *scale, void *stream);
+
+/* Dequantization of blockfp8_quantize_gkn's output, slice by slice; out
+ * [G, K, N] bf16, 16-byte aligned. */
+mxq_status blockfp8_dequantize_gkn(const uint8_t *q, const float *scale, int64_t G, int64_t K,
+                                   int64_t N, int32_t blk, uint16_t *out, void *stream);
+
+/*
  * Block-FP8 with 1 x 128 blocks along each row (the activation recipe):
  * per block of 128 consecutive values of a row (the last one shorter when
  * cols % 128 != 0), S = fl32(amax / 448) and q = E4M3_RNE_sat(fl32(x / S)),

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
                  "mxfp4_dequantize", "mxfp4_fake_quant", "mxq_quantize_colwise_t",
                  "blockfp8_to_mxfp8", "blockfp8_quantize_1x128", "blockfp8_dequantize_1x128",
                  "blockfp8_fake_quant_1x128", "nvfp4_quantize_grouped",
-                 "nvfp4_grouped_workspace_size"]:
+                 "nvfp4_grouped_workspace_size", "blockfp8_quantize_gkn",
+                 "blockfp8_dequantize_gkn"]:
         assert want in names
     assert set(names) == set(mxq.SIGNATURES), "binding and header disagree"
 
@@ -235,6 +236,23 @@ def test_nvfp4_grouped_errors(lib):
     descs[1] = mxq.NvGroupDesc(0x40000, 0, 0x60000, 40, 32, 1, 0)         # NULL q
     assert f(descs, 2, P16, 2, P16, ws, NULL) == mxq.MXQ_EINVAL
     assert f(descs, 0, P16, 0, NULL, 0, NULL) == mxq.MXQ_OK
+
+
+def test_blockfp8_gkn_errors(lib):
+    f = lib.blockfp8_quantize_gkn
+    assert f(P16, -1, 4, 32, 128, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 2, 4, 32, 64, P16, P16, NULL) == mxq.MXQ_ESHAPE        # blk != 128
+    assert f(P16, 2, 4, 36, 128, P16, P16, NULL) == mxq.MXQ_ESHAPE       # N % 8
+    assert f(NULL, 2, 4, 32, 128, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P8, 2, 4, 32, 128, P16, P16, NULL) == mxq.MXQ_EALIGN
+    assert f(P16, 2, 4, 32, 128, P4, P16, NULL) == mxq.MXQ_EALIGN        # q 8-aligned
+    assert f(P16, 2, 4, 32, 128, P16, P2, NULL) == mxq.MXQ_EALIGN        # scale 4-aligned
+    assert f(P16, 2**40, 2**20, 64, 128, P16, P16, NULL) == mxq.MXQ_ESIZE
+    assert f(NULL, 0, 4, 32, 128, NULL, NULL, NULL) == mxq.MXQ_OK
+    d = lib.blockfp8_dequantize_gkn
+    assert d(P16, NULL, 2, 4, 32, 128, P16, NULL) == mxq.MXQ_EINVAL
+    assert d(P16, P16, 2, 4, 32, 128, P8, NULL) == mxq.MXQ_EALIGN
+    assert d(P16, P16, 2, 4, 33, 128, P16, NULL) == mxq.MXQ_ESHAPE
 
 
 def test_mxfp4_errors(lib):
