@@ -214,33 +214,24 @@ __device__ __forceinline__ void mx_colwise_body(
         }
     };
 
-    // one row's row-wise codes, scale byte and fake-quant out
-    auto row_work = [&](int i) __attribute__((always_inline)) {
+    // one row's row-wise codes and scale byte (do_q) and fake-quant (do_fq) out
+    auto row_work = [&](int i, bool do_q, bool do_fq) __attribute__((always_inline)) {
         const int64_t r = r0 + i;
         const bool ok = kFull || (cin && r < rows);
-        const uint32_t sr_b = mx_scale_byte(quad_max(amax8(v[i])));
-        const bool nan_group = sr_b == 0xFFu;
-        const uint32_t lim = mx_limit_bf16(sr_b);
-        const uint32_t l2 = lim | (lim << 16);
-        const float sfr = e8m0_to_f32(sr_b);
-        uint32_t c0 = e4m3x4_row_hw(v[i].x, v[i].y, l2, sfr);
-        uint32_t c1 = e4m3x4_row_hw(v[i].z, v[i].w, l2, sfr);
-        if (nan_group) {
-            c0 = 0x7F7F7F7Fu | signs4(v[i].x, v[i].y);
-            c1 = 0x7F7F7F7Fu | signs4(v[i].z, v[i].w);
+        const MxRow8 m = mx_row_encode8(v[i]);
+        const bool nan_group = m.s == 0xFFu;
+        if (do_q && ok) {
+            st8<kNTStore>(qr + r * cols + col, make_uint2(m.c0, m.c1));
+            sr[r * ngr + (col >> 5)] = (uint8_t)m.s;  // same byte from the 4 lanes of a quad
         }
-        if (kRow && ok) {
-            st8<kNTStore>(qr + r * cols + col, make_uint2(c0, c1));
-            sr[r * ngr + (col >> 5)] = (uint8_t)sr_b;  // same byte from the 4 lanes of a quad
-        }
-        if (kFQRow) {
+        if (do_fq) {
             uint2 lo, hi;
             if (wave_any(nan_group)) {  // rare: a NaN/Inf group in this row of the wave
-                lo = mx_dequant4(c0, (int)sr_b - 7, nan_group);
-                hi = mx_dequant4(c1, (int)sr_b - 7, nan_group);
+                lo = mx_dequant4(m.c0, (int)m.s - 7, nan_group);
+                hi = mx_dequant4(m.c1, (int)m.s - 7, nan_group);
             } else {
-                lo = mx_dequant4_hw(c0, sfr);
-                hi = mx_dequant4_hw(c1, sfr);
+                lo = mx_dequant4_hw(m.c0, m.sf);
+                hi = mx_dequant4_hw(m.c1, m.sf);
             }
             if (ok)
                 st16<kNTStore>(fq_row + r * cols + col, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -308,9 +299,14 @@ __device__ __forceinline__ void mx_colwise_body(
                 }
             }
         }
+    });
+    // then the row-wise work: one stream after the other measured 2.4% faster
+    // on MI355X than interleaving the column and row outputs row by row
+    static_for<0, 32, 2>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
         if (kRowAny) {
-            row_work(i);
-            row_work(i + 1);
+            row_work(i, kRow, kFQRow);
+            row_work(i + 1, kRow, kFQRow);
         }
     });
 }
