@@ -322,10 +322,12 @@ __global__ __launch_bounds__(256) void bfp8_to_mx_kernel(const uint8_t *__restri
 
 // ---------------------------------------------------------------------------
 // NVFP4.  Pass 1: each workgroup writes the max magnitude (bf16 bits) of its
-// share of x to a partials array; pass 2 reduces the partials (an unsigned
-// max: order-independent, deterministic) and quantizes.  In pass 2 a lane
-// pair owns one 16-element block: 16 bytes of x, 4 bytes of packed codes and
-// (both lanes) its scale byte each.
+// share of x to a partials array; one workgroup reduces the partials (an
+// unsigned max: order-independent, deterministic) to g, written to the
+// caller's global-scale word; pass 2 reads g and quantizes.  (Reducing the
+// partials in every encoding workgroup instead cost each of them a 4 KiB read
+// and a barrier.)  In pass 2 a lane pair owns one 16-element block: 16 bytes
+// of x, 4 bytes of packed codes and (both lanes) its scale byte each.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
@@ -333,18 +335,21 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restr
 {
     __shared__ uint32_t red[4];
     constexpr int kU = 8;  // 16-byte loads in flight per thread
+    // each workgroup reads kU * 4 KiB of contiguous x per step, then strides
+    // by the grid (contiguous chunks keep DRAM pages open)
     const uint4 *xv = reinterpret_cast<const uint4 *>(x);
+    constexpr int64_t kChunk = 256 * kU;
     uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + (kU - 1) * stride < nvec; i += kU * stride) {
+    for (int64_t base = (int64_t)blockIdx.x * kChunk; base < nvec; base += (int64_t)gridDim.x * kChunk) {
         uint4 v[kU];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) v[u] = ld16<kNTLoadNvAmax>(xv + i + u * stride);
+        for (int u = 0; u < kU; ++u) {
+            const int64_t i = base + u * 256 + threadIdx.x;
+            v[u] = i < nvec ? ld16<kNTLoadNvAmax>(xv + i) : make_uint4(0, 0, 0, 0);
+        }
 #pragma unroll
         for (int u = 0; u < kU; ++u) m = max(m, amax8(v[u]));
     }
-    for (; i < nvec; i += stride) m = max(m, amax8(ld16<kNTLoadNvAmax>(xv + i)));
     m = wave_max(m);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
     __syncthreads();
@@ -445,15 +450,31 @@ __device__ __forceinline__ void nvfp4_load_rows(const uint16_t *__restrict__ x, 
     }
 }
 
+// One workgroup: the global amax from the partials, g = fl32(A / 2688) (NaN
+// when x holds NaN/Inf), written once for the encoding pass to read.
+__global__ __launch_bounds__(256) void nvfp4_finalize_kernel(const uint32_t *__restrict__ partial,
+                                                             int npartial, float *__restrict__ g_out)
+{
+    __shared__ uint32_t red[4];
+    uint32_t am = 0;
+    for (int k = threadIdx.x; k < npartial; k += 256) am = max(am, partial[k]);
+    am = wave_max(am);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = am;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        am = max(max(red[0], red[1]), max(red[2], red[3]));
+        const bool nonfinite = am >= 0x7F80u;
+        *g_out = nonfinite ? __builtin_nanf("") : __uint_as_float(am << 16) / 2688.0f;  // 448 * 6
+    }
+}
+
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__restrict__ x,
                                                           int64_t rows, int64_t cols,
                                                           uint8_t *__restrict__ q,
                                                           uint8_t *__restrict__ s_out,
-                                                          float *__restrict__ g_out,
-                                                          const uint32_t *__restrict__ partial,
-                                                          int npartial, int64_t nseg)
+                                                          const float *__restrict__ g_in,
+                                                          int64_t nseg)
 {
-    __shared__ uint32_t red[4];
     const int64_t tile = blockIdx.x;
     const int64_t seg = tile % nseg;
     const int64_t rb = tile / nseg;
@@ -461,22 +482,10 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     const int64_t r0 = rb * kRowsNv + wave;
-
-    // issue this wave's loads first, then reduce the amax partials meanwhile
     uint4 v[kRowsNv / 4];
     nvfp4_load_rows<kNTLoadNvQuant>(x, r0, rows, cols, col, v);
-    uint32_t am = 0;
-    for (int k = threadIdx.x; k < npartial; k += 256) am = max(am, partial[k]);
-    am = wave_max(am);
-    if (lane == 0) red[wave] = am;
-    __syncthreads();
-    am = max(max(red[0], red[1]), max(red[2], red[3]));
-
-    const bool nonfinite = am >= 0x7F80u;
-    const float A = __uint_as_float(am << 16);
-    const float g = nonfinite ? __builtin_nanf("") : A / 2688.0f;  // 2688 = 448 * 6
-    if (tile == 0 && threadIdx.x == 0) *g_out = g;
-    nvfp4_encode_rows(v, r0, rows, cols, col, q, s_out, g, nonfinite);
+    const float g = *g_in;
+    nvfp4_encode_rows(v, r0, rows, cols, col, q, s_out, g, g != g);
 }
 
 // ---------------------------------------------------------------------------
@@ -700,14 +709,17 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     if (nvec <= 0) return hipSuccess;
     const int64_t want = (nvec + 255) / 256;
     const int ablocks = (int)(want < kNvAmaxBlocks ? want : kNvAmaxBlocks);
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
     const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(nvfp4_finalize_kernel, dim3(1), dim3(256), 0, stream, ws, ablocks, g);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,
-                       cols, q, s, g, ws, ablocks, nseg);
+                       cols, q, s, g, nseg);
     return hipGetLastError();
 }
 
