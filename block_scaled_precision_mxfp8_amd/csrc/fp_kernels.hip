@@ -527,11 +527,20 @@ __global__ __launch_bounds__(256) void nvfp4_g_reduce_kernel(const int32_t *__re
 {
     __shared__ uint32_t red[4];
     const int32_t j = (int32_t)blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
     uint32_t m = 0;
-    for (int32_t i = 0; i < n; ++i) {  // uniform loop over the entries
-        if (groups[i] != j) continue;
-        const int32_t t1 = i + 1 < n ? starts[i + 1] : total_tiles;
-        for (int32_t k = starts[i] + (int32_t)threadIdx.x; k < t1; k += 256) m = max(m, partial[k]);
+    // 64 entries per step: a ballot finds this group's members (the same mask
+    // in every wave), whose partial ranges the whole workgroup then reduces
+    for (int32_t base = 0; base < n; base += kWave) {
+        const int32_t i = base + lane;
+        uint64_t mask = __ballot(i < n && groups[i] == j);
+        while (mask) {
+            const int32_t k = base + __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int32_t t1 = k + 1 < n ? starts[k + 1] : total_tiles;
+            for (int32_t t = starts[k] + (int32_t)threadIdx.x; t < t1; t += 256)
+                m = max(m, partial[t]);
+        }
     }
     m = wave_max(m);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
