@@ -34,11 +34,12 @@ def orc():
 
 @pytest.fixture(scope="session")
 def gpu():
-    """The HIP library on cuda:0.  Skips only when no GPU is visible; a GPU machine
-    without the built library fails loudly."""
+    """The HIP library on cuda:0.  Skips only when no GPU is visible; with a
+    GPU the library must load (it is built first if missing, and a failed
+    build fails the test loudly: there is no other path)."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible (run with -m gpu on an MI355X)")
     import block_scaled_precision_mxfp8_amd as mxq
-    mxq.load()  # raises if libmxq.so is missing or stale
+    mxq.load()  # raises if libmxq.so cannot be built or loaded
     return mxq
