@@ -219,7 +219,15 @@ def main():
         orc.mxfp8_dequantize(oq, os_, 1)
         dt = time.perf_counter() - t
         sbytes = 2 * se + se + se // 32 + se + ((args.cpu_rows + 31) // 32) * cols + 2 * se
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "host_cores": os.cpu_count(), "cpu_model": model,
                "sample": f"{args.cpu_rows} of {rows} rows of the same batch: row-wise + "
                          f"column-wise quantize and row-wise dequantize (the step's outputs), "
                          f"{dt:.1f} s single-threaded"}
