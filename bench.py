@@ -271,6 +271,12 @@ def main():
         breakdown["act_16384 fake-quant only"] = rotated(
             [lambda d=d: check(lib.mxq_fake_quant(P(d["x"]), rows, cols, 1, P(d["fq"]), sp),
                                "fake_quant") for d in batches], 4 * e)
+        # MXFP8 dequantization of the batches' codes, both axes
+        for ax, qk, sk, nm in ((1, "qr", "sr", "row-wise"), (0, "qc", "sc", "column-wise")):
+            breakdown[f"act_16384 {nm} dequantize"] = rotated(
+                [lambda d=d, ax=ax, qk=qk, sk=sk: check(
+                    lib.mxq_dequantize(P(d[qk]), P(d[sk]), rows, cols, ax, P(d["fq"]), sp),
+                    "dequantize") for d in batches], e + batches[0][sk].numel() + 2 * e)
         # column-wise in the transposed (backward-pass) layout, with and
         # without the row-wise outputs of the same pass
         breakdown["act_16384 one-pass, column-wise transposed"] = rotated(

@@ -428,14 +428,28 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
     const int64_t col = seg * kSeg + lane * 8;
     if (col >= cols) return;  // no barriers below
     const int64_t r0 = rb * kRowsPerTile + wave;
+    // all 8 rows' codes and scales in flight before any is decoded
+    constexpr int kR = kRowsPerTile / 4;
+    uint2 cc[kR], ss[kR];
 #pragma unroll
-    for (int i = 0; i < kRowsPerTile / 4; ++i) {
+    for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
-        if (r >= rows) break;
-        const uint2 c = *reinterpret_cast<const uint2 *>(q + r * cols + col);
+        cc[i] = make_uint2(0, 0);
+        ss[i] = make_uint2(0, 0);
+        if (r < rows) {
+            cc[i] = *reinterpret_cast<const uint2 *>(q + r * cols + col);
+            if (kAxis == 1) ss[i].x = scale[r * (cols >> 5) + (col >> 5)];
+            else ss[i] = *reinterpret_cast<const uint2 *>(scale + (r >> 5) * cols + col);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        const int64_t r = r0 + 4 * i;
+        if (r >= rows) break;  // wave-uniform
+        const uint2 c = cc[i];
         uint32_t b[8];
         if (kAxis == 1) {
-            const uint32_t s = scale[r * (cols >> 5) + (col >> 5)];
+            const uint32_t s = ss[i].x;
             const bool nan = s == 0xFFu;
             // a byte of the form S.1111.111 (NaN code) in either word?
             const uint32_t tx = c.x & 0x7F7F7F7Fu, ty = c.y & 0x7F7F7F7Fu;
@@ -451,17 +465,38 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
             }
             b[0] = lo.x; b[1] = lo.y; b[2] = hi.x; b[3] = hi.y;
         } else {
-            const uint2 sv = *reinterpret_cast<const uint2 *>(scale + (r >> 5) * cols + col);
+            const uint2 sv = ss[i];
+            const uint32_t tx = c.x & 0x7F7F7F7Fu, ty = c.y & 0x7F7F7F7Fu;
+            const bool nan_code = (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
+            // a 0xFF (NaN) scale byte in either word?
+            const bool nan_scale = ((((~sv.x) - 0x01010101u) & sv.x) | (((~sv.y) - 0x01010101u) & sv.y)) &
+                                   0x80808080u;
             uint32_t w[4];
+            if (wave_any(nan_code || nan_scale)) {
 #pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                const uint32_t cw = j < 4 ? c.x : c.y;
-                const uint32_t sw = j < 4 ? sv.x : sv.y;
-                const int sh = 8 * (j & 3);
-                const uint32_t s0 = (sw >> sh) & 0xFFu, s1 = (sw >> (sh + 8)) & 0xFFu;
-                const uint32_t d0 = mx_dequant1((cw >> sh) & 0xFFu, (int)s0 - 7, s0 == 0xFFu);
-                const uint32_t d1 = mx_dequant1((cw >> (sh + 8)) & 0xFFu, (int)s1 - 7, s1 == 0xFFu);
-                w[j / 2] = d0 | (d1 << 16);
+                for (int j = 0; j < 8; j += 2) {
+                    const uint32_t cw = j < 4 ? c.x : c.y;
+                    const uint32_t sw = j < 4 ? sv.x : sv.y;
+                    const int sh = 8 * (j & 3);
+                    const uint32_t s0 = (sw >> sh) & 0xFFu, s1 = (sw >> (sh + 8)) & 0xFFu;
+                    const uint32_t d0 = mx_dequant1((cw >> sh) & 0xFFu, (int)s0 - 7, s0 == 0xFFu);
+                    const uint32_t d1 = mx_dequant1((cw >> (sh + 8)) & 0xFFu, (int)s1 - 7,
+                                                    s1 == 0xFFu);
+                    w[j / 2] = d0 | (d1 << 16);
+                }
+            } else {
+                // one scale per column: E4M3 -> fp32 exactly (v_cvt_pk_f32_fp8), times
+                // the column's power of two (exact, subnormals kept), bf16 RNE
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t cw = h ? c.y : c.x, sw = h ? sv.y : sv.x;
+                    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, false);
+                    const f32x2 bb = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw, true);
+                    w[2 * h] = bf16x2_rne(a.x * e8m0_to_f32(sw & 0xFFu),
+                                          a.y * e8m0_to_f32((sw >> 8) & 0xFFu));
+                    w[2 * h + 1] = bf16x2_rne(bb.x * e8m0_to_f32((sw >> 16) & 0xFFu),
+                                              bb.y * e8m0_to_f32(sw >> 24));
+                }
             }
             b[0] = w[0]; b[1] = w[1]; b[2] = w[2]; b[3] = w[3];
         }
