@@ -430,18 +430,26 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
     const int64_t r0 = rb * kRowsPerTile + wave;
     // all 8 rows' codes and scales in flight before any is decoded
     constexpr int kR = kRowsPerTile / 4;
-    uint2 cc[kR], ss[kR];
+    uint2 cc[kR];
+    uint32_t ss[kR];
+    // column groups: the tile's 32 rows are one group row, so one scale load
+    static_assert(kRowsPerTile == 32, "a dequantize tile spans exactly one column-group row");
+    const uint2 sv = kAxis == 0 && r0 < rows
+                         ? *reinterpret_cast<const uint2 *>(scale + rb * cols + col)
+                         : make_uint2(0, 0);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
         cc[i] = make_uint2(0, 0);
-        ss[i] = make_uint2(0, 0);
+        ss[i] = 0u;
         if (r < rows) {
             cc[i] = *reinterpret_cast<const uint2 *>(q + r * cols + col);
-            if (kAxis == 1) ss[i].x = scale[r * (cols >> 5) + (col >> 5)];
-            else ss[i] = *reinterpret_cast<const uint2 *>(scale + (r >> 5) * cols + col);
+            if (kAxis == 1) ss[i] = scale[r * (cols >> 5) + (col >> 5)];
         }
     }
+    // a 0xFF (NaN) scale byte among the column scales?
+    const bool nan_scale = ((((~sv.x) - 0x01010101u) & sv.x) | (((~sv.y) - 0x01010101u) & sv.y)) &
+                           0x80808080u;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
         const uint2 c = cc[i];
         uint32_t b[8];
         if (kAxis == 1) {
-            const uint32_t s = ss[i].x;
+            const uint32_t s = ss[i];
             const bool nan = s == 0xFFu;
             // a byte of the form S.1111.111 (NaN code) in either word?
             const uint32_t tx = c.x & 0x7F7F7F7Fu, ty = c.y & 0x7F7F7F7Fu;
@@ -465,12 +473,8 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
             }
             b[0] = lo.x; b[1] = lo.y; b[2] = hi.x; b[3] = hi.y;
         } else {
-            const uint2 sv = ss[i];
             const uint32_t tx = c.x & 0x7F7F7F7Fu, ty = c.y & 0x7F7F7F7Fu;
             const bool nan_code = (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
-            // a 0xFF (NaN) scale byte in either word?
-            const bool nan_scale = ((((~sv.x) - 0x01010101u) & sv.x) | (((~sv.y) - 0x01010101u) & sv.y)) &
-                                   0x80808080u;
             uint32_t w[4];
             if (wave_any(nan_code || nan_scale)) {
 #pragma unroll
