@@ -142,10 +142,15 @@ def _as_2d_rows(x: torch.Tensor) -> torch.Tensor:
 # MXFP8
 # ---------------------------------------------------------------------------
 
-def quantize_rowwise(x: torch.Tensor, fake_quant: bool = False):
+def quantize_rowwise(x: torch.Tensor, fake_quant: bool = False, scale_pad=None):
     """Row-wise MXFP8 of a 2-D bf16 tensor (row stride may exceed cols).
     Returns (q uint8 [rows, cols], scale uint8 [rows, cols/32]) and, with
-    fake_quant, the bf16 dequantization of that result as a third tensor."""
+    fake_quant, the bf16 dequantization of that result as a third tensor.
+
+    scale_pad=(rm, cm) returns the scale in a zero-filled buffer of
+    [roundup(rows, rm), roundup(cols/32, cm)] bytes (the padded scale tiles
+    some GEMM consumers read); its top-left [rows, cols/32] is the compact
+    scale, written through the scale leading dimension."""
     _need_bf16_cuda(x)
     if x.dim() != 2:
         raise ValueError("quantize_rowwise expects a 2-D tensor; use mxfp8_quantize for N-D")
@@ -153,8 +158,15 @@ def quantize_rowwise(x: torch.Tensor, fake_quant: bool = False):
         x = x.contiguous()
     rows, cols = x.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
-    s = torch.empty((rows, cols // MX_GROUP if cols % MX_GROUP == 0 else 0), dtype=torch.uint8,
-                    device=x.device)
+    ng = cols // MX_GROUP if cols % MX_GROUP == 0 else 0
+    if scale_pad is None:
+        s = torch.empty((rows, ng), dtype=torch.uint8, device=x.device)
+    else:
+        rm, cm = (int(v) for v in scale_pad)
+        if rm < 1 or cm < 1:
+            raise ValueError("scale_pad entries must be positive")
+        s = torch.zeros((-(-rows // rm) * rm, -(-ng // cm) * cm), dtype=torch.uint8,
+                        device=x.device)
     fq = torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device) if fake_quant else None
     st = load().mxq_quantize_rowwise(_ptr(x), rows, cols, x.stride(0), _ptr(q), cols, _ptr(s),
                                      s.shape[1], _ptr(fq), cols, _stream(x))

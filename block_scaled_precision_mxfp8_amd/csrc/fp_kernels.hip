@@ -397,16 +397,36 @@ __device__ __forceinline__ uint32_t nvfp4_codes8(const uint4 a, float eff, float
 // Tiles: 512-column segment x 32 rows (4 waves x 8 rows).  Lane pair
 // (2k, 2k+1) holds one 16-element block, 8 elements each, so every load and
 // store instruction of a wave is contiguous; the block amax is one DPP swap.
+//
+// With g fixed for the workgroup, a block's effective scale can take only 127
+// values, one per E4M3 magnitude code: the workgroup tabulates
+// eff = fl32(val(m) * g) and RN(1 / eff) once (one IEEE division per entry)
+// in LDS, so a block looks its pair up instead of dividing.  Every thread of
+// the workgroup must call this (it holds a barrier).
+__device__ __forceinline__ void nvfp4_scale_table(float2 *tab, float g)
+{
+    if (threadIdx.x < 128) {
+        const float eff = e4m3_mag_value(threadIdx.x) * g;  // one IEEE fp32 multiplication
+        tab[threadIdx.x] = make_float2(eff, markstein_ok(eff) ? 1.0f / eff : 0.0f);
+    }
+    __syncthreads();
+}
+
 // The per-block steps for one wave's 8 rows of a tile (rows r0 + 4i), given
-// the global scale g (NaN when the tensor or scale group holds NaN/Inf).
+// the global scale g (NaN when the tensor or scale group holds NaN/Inf) and
+// the workgroup's table for g.  The block-scale quotient b / (6g) is IEEE
+// division's result either way: by the reciprocal-FMA step when 6g lies in
+// its proven domain (b <= A keeps the quotient under 449), else by division.
 __device__ __forceinline__ void nvfp4_encode_rows(const uint4 (&v)[kRowsNv / 4], int64_t r0,
                                                   int64_t rows, int64_t cols, int64_t col,
                                                   uint8_t *__restrict__ q,
                                                   uint8_t *__restrict__ s_out, float g,
-                                                  bool nonfinite)
+                                                  bool nonfinite, const float2 *tab)
 {
     const bool cin = col < cols;  // cols % 16 == 0: a block (lane pair) is all in or all out
     const float d = 6.0f * g;
+    const bool dfast = markstein_ok(d);           // uniform: g is the workgroup's
+    const float yd = dfast ? 1.0f / d : 0.0f;     // RN(1 / d), one IEEE division per thread
 #pragma unroll
     for (int i = 0; i < kRowsNv / 4; ++i) {
         const int64_t r = r0 + 4 * i;
@@ -419,12 +439,14 @@ __device__ __forceinline__ void nvfp4_encode_rows(const uint4 (&v)[kRowsNv / 4],
         } else if (g == 0.0f) {
             s = 0u;
         } else {
-            const float ratio = __uint_as_float(b << 16) / d;  // one IEEE fp32 division
+            const float bf = __uint_as_float(b << 16);
+            const float ratio = dfast ? div_markstein(bf, d, yd) : bf / d;
             s = e4m3_mag_from_f32(ratio);
         }
-        const float eff = e4m3_mag_value(s & 0x7Fu) * g;       // one IEEE fp32 multiplication
+        const float2 t = tab[s & 0x7Fu];
+        const float eff = t.x;
         const bool fast = !wave_any(nonfinite || !markstein_ok(eff));
-        const float y = fast ? 1.0f / eff : 0.0f;
+        const float y = t.y;
         const uint32_t codes = fast ? nvfp4_codes8(v[i], eff, y, true, false)
                                     : nvfp4_codes8(v[i], eff, 0.0f, false, nonfinite);
         if (ok) {
@@ -482,10 +504,12 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     const int64_t r0 = rb * kRowsNv + wave;
+    __shared__ float2 tab[128];
     uint4 v[kRowsNv / 4];
     nvfp4_load_rows<kNTLoadNvQuant>(x, r0, rows, cols, col, v);
     const float g = *g_in;
-    nvfp4_encode_rows(v, r0, rows, cols, col, q, s_out, g, g != g);
+    nvfp4_scale_table(tab, g);
+    nvfp4_encode_rows(v, r0, rows, cols, col, q, s_out, g, g != g, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -563,10 +587,12 @@ __global__ __launch_bounds__(256) void nvfp4_g_quant_kernel(const NvEntry *__res
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t col = seg * kSegNv + lane * 8, r0 = rb * kRowsNv + wave;
+    __shared__ float2 tab[128];
     uint4 v[kRowsNv / 4];
     nvfp4_load_rows<kNTLoadNvQuant>(E.x, r0, E.rows, E.cols, col, v);
     const float g = gs[E.group];
-    nvfp4_encode_rows(v, r0, E.rows, E.cols, col, E.q, E.s, g, g != g);
+    nvfp4_scale_table(tab, g);
+    nvfp4_encode_rows(v, r0, E.rows, E.cols, col, E.q, E.s, g, g != g, tab);
 }
 
 // 8 packed E2M1 nibbles (one word) -> 8 bf16, effective scale eff.

@@ -119,6 +119,23 @@ def test_rowwise_strided_with_guard_bands(gpu, orc, ldq):
     assert np.all(fm[:, cols:] == 0x5A5A)
 
 
+@pytest.mark.parametrize("rows,cols", [(4097, 224), (200, 96), (128, 128)])
+def test_rowwise_padded_scale_tiles(gpu, orc, rows, cols):
+    """Scales written into a zero-filled [roundup(rows, 128), roundup(cols/32, 4)]
+    buffer: the compact scale sits top-left, every pad byte stays 0."""
+    announce(f"rowwise padded scale {rows}x{cols}")
+    xb = workloads.random_bf16((rows, cols), rows + cols)
+    q, s = gpu.quantize_rowwise(to_dev_bf16(xb), scale_pad=(128, 4))
+    torch.cuda.synchronize()
+    oq, os_ = orc.mxfp8_quantize_rowwise(xb)
+    ng = cols // 32
+    assert s.shape == ((rows + 127) // 128 * 128, (ng + 3) // 4 * 4)
+    sh = u8(s)
+    assert_same("padded q", u8(q), oq)
+    assert_same("padded scale", sh[:rows, :ng], os_)
+    assert not sh[rows:].any() and not sh[:, ng:].any()
+
+
 def test_mxfp8_quantize_adapter_and_param_names(gpu, orc):
     xb = workloads.random_bf16((2 * 48, 64), 9)
     announce("adapter 3-D")
