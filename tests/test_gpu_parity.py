@@ -267,6 +267,25 @@ def test_dequant_hw_path_all_finite_pairs(gpu, orc):
     assert_same("dequant hw path", bits16(out), orc.mxfp8_dequantize(q, s, 1))
 
 
+def test_dequant_colwise_hw_path_all_finite_pairs(gpu, orc):
+    """Column groups, no NaN code or scale anywhere (the hardware-decode path):
+    every non-NaN code meets every finite scale byte in every column, and the
+    scale changes from column to column."""
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)   # 254
+    G, cols = 255 * 8, 256
+    g = np.arange(G)[:, None]
+    s = ((g + np.arange(cols)[None, :]) % 255).astype(np.uint8)                      # [G, cols]
+    j = np.arange(32)[None, :]
+    idx = (32 * (np.arange(G)[:, None] // 255) + j) % 254                            # [G, 32]
+    q = np.repeat(finite[idx].reshape(G * 32, 1), cols, axis=1)                      # [32G, cols]
+    pairs = set(zip(np.repeat(s, 32, axis=0)[:, 0].tolist(), q[:, 0].tolist()))
+    assert len(pairs) == 255 * 254  # column 0 alone already sees every pair
+    announce("dequant colwise hw path")
+    out = gpu.dequantize(torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda(), axis=0)
+    torch.cuda.synchronize()
+    assert_same("dequant colwise hw path", bits16(out), orc.mxfp8_dequantize(q, s, 0))
+
+
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("shape", [(256, 512), (33, 64), (100, 7168)])
 def test_fake_quant(gpu, orc, axis, shape):
