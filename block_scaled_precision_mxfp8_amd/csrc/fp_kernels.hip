@@ -23,12 +23,15 @@ constexpr int kRowsNv = 32; // NVFP4 rows per workgroup tile
 // Streaming (non-temporal) hints, chosen by measurement on MI355X with
 // inputs read cold from HBM.  Outputs are written once.  Hinted 16-byte loads
 // of x help block-FP8 (+3%); the dequantizers' 4- and 8-byte code loads do
-// better unhinted (NVFP4: 4.3 -> 5.0 TB/s).  The NVFP4 amax pass loads
-// unhinted so that x can stay in the Infinity Cache for the encoding pass.
+// better unhinted (NVFP4: 4.3 -> 5.0 TB/s).  The single-tensor NVFP4 amax
+// pass loads unhinted so that x can stay in the Infinity Cache for the
+// encoding pass; the grouped amax pass streams (its tensors together far
+// exceed that cache: 2.87 -> 2.72 ms on 256 MoE gate/up tensors).
 constexpr bool kNTStore = true;
 constexpr bool kNTLoad = true;
 constexpr bool kNTLoadDq = false;
 constexpr bool kNTLoadNvAmax = false;
+constexpr bool kNTLoadNvGAmax = true;
 constexpr bool kNTLoadNvQuant = true;
 
 // 8 bf16 -> 8 E4M3 codes of fl32(x / div): by reciprocal + FMA correction
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(256) void nvfp4_g_amax_kernel(const NvEntry *__rest
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     uint4 v[kRowsNv / 4];
-    nvfp4_load_rows<kNTLoadNvAmax>(E.x, rb * kRowsNv + wave, E.rows, E.cols, seg * kSegNv + lane * 8,
+    nvfp4_load_rows<kNTLoadNvGAmax>(E.x, rb * kRowsNv + wave, E.rows, E.cols, seg * kSegNv + lane * 8,
                                    v);
     uint32_t m = 0;
 #pragma unroll
