@@ -42,6 +42,22 @@ def test_colwise_t_output_subsets(gpu, orc, rowwise, fake_quant):
     check_colwise_t(gpu, orc, workloads.random_bf16((200, 1056), 77), "subset", rowwise, fake_quant)
 
 
+@pytest.mark.parametrize("shape", [(4229, 1056), (8192, 512), (130, 7168)])
+def test_colwise_t_column_only_band_units(gpu, orc, shape):
+    """Column-only launches order workgroups in units of 32 row bands per XCD:
+    a partial last unit (4229 rows = 33 bands + 5 rows), exactly 2 units,
+    and fewer bands than one unit over many segments."""
+    check_colwise_t(gpu, orc, workloads.random_bf16(shape, shape[0] + 7 * shape[1]),
+                    f"t-col-only{shape}", rowwise=False, fake_quant=False)
+
+
+def test_colwise_t_act_16384_column_only(gpu, orc):
+    """The [16384, 7168] activation, transposed column-wise only (the bench's
+    column-only launch), every output byte."""
+    check_colwise_t(gpu, orc, workloads.act_16384(), "act_16384 col-only", rowwise=False,
+                    fake_quant=False)
+
+
 def test_colwise_t_edge_values(gpu, orc):
     """Every (value, reachable scale) sweep group laid down a column, plus
     NaN and Inf columns."""
