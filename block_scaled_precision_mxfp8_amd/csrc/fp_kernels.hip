@@ -637,9 +637,8 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__res
                                                             uint16_t *__restrict__ out,
                                                             int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg;
-    const int64_t rb = tile / nseg;
+    int64_t seg, rb;
+    if (!xcd_row_tile(nseg, (rows + kRowsNv - 1) / kRowsNv, seg, rb)) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
@@ -793,8 +792,9 @@ hipError_t launch_nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float 
                                 int64_t cols, uint16_t *out, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
-    if (tiles <= 0) return hipSuccess;
+    const int64_t nrb = (rows + kRowsNv - 1) / kRowsNv;
+    if (nseg <= 0 || nrb <= 0) return hipSuccess;
+    const int64_t tiles = xcd_row_grid(nseg, nrb);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, s, g,
                        rows, cols, out, nseg);

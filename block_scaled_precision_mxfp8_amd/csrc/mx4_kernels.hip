@@ -95,8 +95,8 @@ __global__ __launch_bounds__(256) void mx4_dequant_kernel(const uint8_t *__restr
                                                           int64_t rows, int64_t cols,
                                                           uint16_t *__restrict__ out, int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg, rb = tile / nseg;
+    int64_t seg, rb;
+    if (!xcd_row_tile(nseg, (rows + kRows4 - 1) / kRows4, seg, rb)) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSeg4 + lane * 8;
@@ -152,8 +152,9 @@ hipError_t launch_mx4_dequant(const uint8_t *q, const uint8_t *scale, int64_t ro
                               uint16_t *out, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSeg4 - 1) / kSeg4;
-    const int64_t tiles = nseg * ((rows + kRows4 - 1) / kRows4);
-    if (tiles <= 0) return hipSuccess;
+    const int64_t nrb = (rows + kRows4 - 1) / kRows4;
+    if (nseg <= 0 || nrb <= 0) return hipSuccess;
+    const int64_t tiles = xcd_row_grid(nseg, nrb);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(mx4_dequant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scale,
                        rows, cols, out, nseg);
