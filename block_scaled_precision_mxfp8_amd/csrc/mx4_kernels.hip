@@ -79,8 +79,16 @@ __global__ __launch_bounds__(256) void mx4_quant_kernel(const uint16_t *__restri
                                                         uint8_t *__restrict__ scale,
                                                         uint16_t *__restrict__ fq, int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg, rb = tile / nseg;
+    // quantize-only: row blocks per XCD, so the 16-byte pieces of each scale
+    // line are written back from one L2 (+2% on MI355X; with the bf16
+    // fake-quant output the plain order measured 1% faster)
+    int64_t seg, rb;
+    if (kQ && !kFQ) {
+        if (!xcd_row_tile(nseg, (rows + kRows4 - 1) / kRows4, seg, rb)) return;
+    } else {
+        seg = blockIdx.x % nseg;
+        rb = blockIdx.x / nseg;
+    }
     if ((seg + 1) * kSeg4 <= cols && (rb + 1) * kRows4 <= rows)
         mx4_tile<kQ, kFQ, true>(x, rows, cols, q, scale, fq, seg, rb);
     else
@@ -132,8 +140,9 @@ hipError_t launch_mx4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8
                             uint8_t *scale, uint16_t *fq, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSeg4 - 1) / kSeg4;
-    const int64_t tiles = nseg * ((rows + kRows4 - 1) / kRows4);
-    if (tiles <= 0) return hipSuccess;
+    const int64_t nrb = (rows + kRows4 - 1) / kRows4;
+    if (nseg <= 0 || nrb <= 0) return hipSuccess;
+    const int64_t tiles = (q && !fq) ? xcd_row_grid(nseg, nrb) : nseg * nrb;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);
     if (q && fq)

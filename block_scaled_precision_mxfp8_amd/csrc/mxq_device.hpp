@@ -66,12 +66,13 @@ __device__ __forceinline__ uint32_t dpp_swap2(uint32_t v)
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
 }
 
-// Row-block-per-XCD tile order for dequantizers whose per-row scale bytes are
-// a short piece (16 or 32 bytes) of a 128-byte line per 512-column segment.
+// Row-block-per-XCD tile order for kernels whose per-row scale bytes are a
+// short piece (16 or 32 bytes) of a 128-byte line per 512-column segment.
 // Workgroup i runs on XCD i % 8.  Row block rb goes to XCD rb % 8, and its
-// segments run there one after another, so each scale line is fetched by one
-// L2 instead of by several (HBM reads of MXFP4 dequantization were +36% over
-// the algorithmic bytes, NVFP4's +34%; the order gains 7-12% on MI355X).  The
+// segments run there one after another, so each scale line is fetched (or
+// written back) by one L2 instead of by several (HBM reads of MXFP4
+// dequantization were +36% over the algorithmic bytes, NVFP4's +34%; the
+// order gains 7-12% there on MI355X).  The
 // grid has xcd_row_grid(nseg, nrb) workgroups; the padding ones (rb >= nrb)
 // get false.
 __host__ __device__ inline int64_t xcd_row_grid(int64_t nseg, int64_t nrb)
