@@ -299,3 +299,60 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "oracle" not in text.replace("oracle-free", ""), f
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include "mxq.h"
+
+#define EXPECT(call, want) do { mxq_status s_ = (call); if (s_ != (want)) { \
+    printf("line %d: got %d (%s), want %d\n", __LINE__, (int)s_, mxq_status_string(s_), \
+           (int)(want)); return 1; } } while (0)
+
+int main(void)
+{
+    const uint16_t *x = (const uint16_t *)0x10000;   /* never dereferenced: every */
+    uint8_t *q = (uint8_t *)0x10000;                 /* call fails validation     */
+    uint16_t *o = (uint16_t *)0x10000;
+    float *f = (float *)0x10000;
+    int st;
+    if (mxq_abi_version() != MXQ_ABI_VERSION) return 2;
+    for (st = 0; st <= 5; ++st)
+        if (!mxq_status_string(st)) return 3;
+    EXPECT(mxq_quantize_rowwise(x, 4, 33, 33, q, 33, q, 1, NULL, 0, NULL), MXQ_ESHAPE);
+    EXPECT(mxq_quantize_rowwise(x, 0, 32, 32, NULL, 32, NULL, 1, NULL, 0, NULL), MXQ_OK);
+    EXPECT(mxq_quantize_colwise(NULL, 4, 32, q, q, NULL, NULL, NULL, NULL), MXQ_EINVAL);
+    EXPECT(mxq_quantize_colwise_t(x, 4, 32, q, 2, q, NULL, NULL, NULL, NULL), MXQ_ESHAPE);
+    EXPECT(mxq_dequantize(q, q, 4, 32, 2, o, NULL), MXQ_EINVAL);
+    EXPECT(mxq_fake_quant(x, 4, 48, 1, o, NULL), MXQ_ESHAPE);
+    EXPECT(mxq_quantize_rowwise_grouped(NULL, -1, NULL, 0, NULL), MXQ_EINVAL);
+    EXPECT(blockfp8_quantize(x, 4, 32, 64, q, f, NULL), MXQ_ESHAPE);
+    EXPECT(blockfp8_dequantize(q, f, -4, 32, 128, o, NULL), MXQ_EINVAL);
+    EXPECT(blockfp8_quantize_1x128(x, 4, 12, q, f, NULL, NULL), MXQ_ESHAPE);
+    EXPECT(blockfp8_to_mxfp8(q, f, 4, 48, 128, q, q, NULL), MXQ_ESHAPE);
+    EXPECT(mxfp4_quantize(x, 4, 16, q, q, NULL, NULL), MXQ_ESHAPE);
+    EXPECT(nvfp4_quantize(x, 4, 24, q, q, f, q, nvfp4_workspace_size(), NULL), MXQ_ESHAPE);
+    EXPECT(nvfp4_quantize(x, 4, 32, q, q, f, q, 0, NULL), MXQ_ESIZE);
+    EXPECT(nvfp4_dequantize(q, q, f, 4, 32, (uint16_t *)0x10002, NULL), MXQ_EALIGN);
+    printf("c client ok\n");
+    return 0;
+}
+"""
+
+
+def test_c_client_builds_links_and_gets_errors(tmp_path):
+    """A plain C99 program includes include/mxq.h, links libmxq.so and gets
+    the documented status codes back (argument checks run before any HIP call,
+    so this needs no GPU): the header is valid C and the symbols unmangled."""
+    if not os.path.exists(mxq.LIB_PATH):
+        pytest.fail("libmxq.so is not built (run __graft_entry__.build())")
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(mxq.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lmxq",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "c client ok" in r.stdout
