@@ -48,6 +48,7 @@ SIGNATURES = {
     "mxq_quantize_colwise_t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
     "mxq_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
     "mxq_fake_quant": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
+    "mxq_e8m0_to_fp32": (ctypes.c_int, [_vp, _i64, _vp, _vp]),
     "mxq_grouped_workspace_size": (_sz, [_i32]),
     "mxq_quantize_rowwise_grouped": (ctypes.c_int, [_vp, _i32, _vp, _sz, _vp]),
     "blockfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _vp, _vp]),
@@ -516,6 +517,20 @@ def nvfp4_dequantize(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor) -> torch
 # ---------------------------------------------------------------------------
 # MXFP8 export adapter ("PR #1935 完整报告", 实现拆解 item 1; 关键源码片段)
 # ---------------------------------------------------------------------------
+
+def e8m0_to_fp32(scale: torch.Tensor) -> torch.Tensor:
+    """E8M0 scale bytes (uint8 or float8_e8m0fnu, any shape) as fp32 values
+    2^(b - 127), NaN for 0xFF: the fp32 scale storage some consumers require."""
+    if not isinstance(scale, torch.Tensor) or not scale.is_cuda:
+        raise ValueError("scale must be a GPU tensor (the library has no CPU path)")
+    if scale.dtype != torch.uint8:
+        scale = scale.view(torch.uint8)
+    scale = scale.contiguous()
+    out = torch.empty(scale.shape, dtype=torch.float32, device=scale.device)
+    st = load().mxq_e8m0_to_fp32(_ptr(scale), scale.numel(), _ptr(out), _stream(scale))
+    _check("mxq_e8m0_to_fp32", st)
+    return out
+
 
 def mxfp8_quantize(weight: torch.Tensor):
     """Row-wise MXFP8 of any [..., cols] bf16 tensor, flattened to 2-D:

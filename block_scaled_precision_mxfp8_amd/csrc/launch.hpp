@@ -32,6 +32,8 @@ hipError_t launch_mx_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, ui
                                int64_t ldt, uint8_t *st, uint8_t *qr, uint8_t *sr,
                                uint16_t *fq_row, hipStream_t stream);
 
+hipError_t launch_e8m0_to_f32(const uint8_t *scale, int64_t n, float *out, hipStream_t stream);
+
 hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
                              int axis, uint16_t *out, hipStream_t stream);
 

@@ -635,6 +635,26 @@ hipError_t launch_mx_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, ui
     return hipGetLastError();
 }
 
+// E8M0 bytes -> fp32 values (2^(b - 127), 0xFF -> quiet NaN), grid-stride.
+__global__ __launch_bounds__(256) void e8m0_to_f32_kernel(const uint8_t *__restrict__ s,
+                                                          int64_t n, float *__restrict__ out)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * 256) {
+        const uint32_t b = s[i];
+        out[i] = b == 0xFFu ? __uint_as_float(0x7FC00000u) : e8m0_to_f32(b);
+    }
+}
+
+hipError_t launch_e8m0_to_f32(const uint8_t *scale, int64_t n, float *out, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    const int64_t want = (n + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(e8m0_to_f32_kernel, dim3(blocks), dim3(256), 0, stream, scale, n, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
                              int axis, uint16_t *out, hipStream_t stream)
 {

@@ -113,6 +113,15 @@ mxq_status mxq_dequantize(const uint8_t *q, const uint8_t *scale, int64_t rows, 
     return from_hip(mxq::launch_mx_dequant(q, scale, rows, cols, axis, out, as_stream(stream)));
 }
 
+mxq_status mxq_e8m0_to_fp32(const uint8_t *scale, int64_t n, float *out, void *stream)
+{
+    if (n < 0) return MXQ_EINVAL;
+    if (n == 0) return MXQ_OK;
+    if (!scale || !out) return MXQ_EINVAL;
+    if (!aligned(out, 4)) return MXQ_EALIGN;
+    return from_hip(mxq::launch_e8m0_to_f32(scale, n, out, as_stream(stream)));
+}
+
 mxq_status mxq_fake_quant(const uint16_t *x, int64_t rows, int64_t cols, int axis, uint16_t *out,
                           void *stream)
 {

@@ -136,6 +136,17 @@ mxq_status mxq_dequantize(const uint8_t *q, const uint8_t *scale, int64_t rows, 
                           int axis, uint16_t *out, void *stream);
 
 /*
+ * E8M0 scale bytes as fp32 values, for consumers that take fp32 scales only
+ * (miles PR #1372 "V4 mxfp4", PR description: scale storage forced to fp32
+ * for fp8_simulate; E8M0 per the OCP microscaling definition):
+ * out[i] = 2^(scale[i] - 127), exact (byte 0 gives the fp32 subnormal
+ * 2^-127); byte 0xFF (NaN) gives the quiet NaN 0x7FC00000.
+ *   scale  n bytes, any alignment     out  n floats, 4-byte aligned
+ * Works for MXFP8 and MXFP4 scales of either axis (any layout: elementwise).
+ */
+mxq_status mxq_e8m0_to_fp32(const uint8_t *scale, int64_t n, float *out, void *stream);
+
+/*
  * MXFP8 fake quantization (simulated QAT, miles PR #1372 "V4 mxfp4"):
  * out = dequantize(quantize(x)) along `axis` (1 = row-wise groups, 0 =
  * column-wise), written as bf16 without materializing the codes.

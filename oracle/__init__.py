@@ -142,6 +142,13 @@ class Oracle:
     def e8m0_to_double(self, b: int) -> float:
         return self.L.orc_e8m0_to_double(int(b))
 
+    def e8m0_to_fp32(self, scale: np.ndarray) -> np.ndarray:
+        """E8M0 bytes as fp32 values (the fp32 scale storage of "V4 mxfp4"'s
+        PR description): each byte's exact value 2^(b - 127), NaN for 0xFF.
+        Every such value is exact in fp32 (2^-127 as a subnormal)."""
+        table = np.array([self.e8m0_to_double(b) for b in range(256)], dtype=np.float64)
+        return table.astype(np.float32)[np.asarray(scale, dtype=np.uint8)]
+
     def e2m1_to_double(self, n: int) -> float:
         return self.L.orc_e2m1_to_double(int(n))
 

@@ -356,3 +356,12 @@ def test_c_client_builds_links_and_gets_errors(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "c client ok" in r.stdout
+
+
+def test_e8m0_to_fp32_errors(lib):
+    f = lib.mxq_e8m0_to_fp32
+    assert f(P16, -1, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 0, NULL, NULL) == mxq.MXQ_OK
+    assert f(NULL, 8, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 8, NULL, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 8, P2, NULL) == mxq.MXQ_EALIGN

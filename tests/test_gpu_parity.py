@@ -286,6 +286,23 @@ def test_dequant_colwise_hw_path_all_finite_pairs(gpu, orc):
     assert_same("dequant colwise hw path", bits16(out), orc.mxfp8_dequantize(q, s, 0))
 
 
+def test_e8m0_to_fp32_all_bytes_and_real_scales(gpu, orc):
+    """The fp32 scale view: all 256 bytes, then the row scales of a real
+    quantization (odd element count, float8_e8m0fnu input view)."""
+    announce("e8m0 -> fp32")
+    allb = torch.arange(256, dtype=torch.int32).to(torch.uint8).cuda()
+    got = f32bits(gpu.e8m0_to_fp32(allb))
+    want = f32bits(orc.e8m0_to_fp32(np.arange(256, dtype=np.uint8)))
+    assert got[255] == 0x7FC00000
+    assert_same("e8m0 all bytes", got[:255], want[:255])
+    xb = workloads.random_bf16((37, 7168 - 32), 61)
+    _, s = gpu.quantize_rowwise(to_dev_bf16(xb))
+    got = gpu.e8m0_to_fp32(s.view(torch.float8_e8m0fnu))
+    torch.cuda.synchronize()
+    assert got.shape == s.shape and got.dtype == torch.float32
+    assert_same("e8m0 real scales", f32bits(got), f32bits(orc.e8m0_to_fp32(u8(s))))
+
+
 @pytest.mark.parametrize("axis", [0, 1])
 @pytest.mark.parametrize("shape", [(256, 512), (33, 64), (100, 7168)])
 def test_fake_quant(gpu, orc, axis, shape):

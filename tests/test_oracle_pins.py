@@ -19,6 +19,18 @@ def test_e8m0_decode(orc):
     pins.pin_e8m0_decode(orc)
 
 
+def test_e8m0_to_fp32_matches_torch_cast(orc):
+    """The fp32 scale view against torch's float8_e8m0fnu -> float32 cast, all
+    256 bytes (NaN for 0xFF, the subnormal 2^-127 for 0)."""
+    import torch
+    want = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu).float()
+    got = orc.e8m0_to_fp32(np.arange(256, dtype=np.uint8))
+    w = want.numpy()
+    assert np.isnan(got[255]) and np.isnan(w[255])
+    assert np.array_equal(got[:255].view(np.uint32), w[:255].view(np.uint32))
+    assert got[0].view(np.uint32) == 0x00400000 and got[127] == 1.0
+
+
 def test_e2m1_decode(orc):
     pins.pin_e2m1_decode(orc)
 
