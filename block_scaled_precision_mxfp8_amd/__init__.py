@@ -6,13 +6,20 @@ stream; every step of every quantizer runs in the library's HIP kernels.
 There is no CPU fallback: without the built library on a GPU every call raises.
 
 Entry points (names follow the C ABI):
-  quantize_rowwise(x, fake_quant=False)          -> q, scale[, fq]
-  quantize_colwise(x, rowwise=True, fake_quant=True)
-  dequantize(q, scale, axis=1)                   -> bf16
-  fake_quant(x, axis=1)                          -> bf16
-  quantize_rowwise_grouped([x0, x1, ...])        -> [(q, scale), ...]
-  blockfp8_quantize(x, blk=128) / blockfp8_dequantize(q, S, blk=128)
-  nvfp4_quantize(x) / nvfp4_dequantize(q, s, g)
+  MXFP8   quantize_rowwise(x, fake_quant=False, scale_pad=None) -> q, scale[, fq]
+          quantize_colwise(x, rowwise=True, fake_quant=True)   one read of x
+          quantize_colwise_t(x, rowwise=True, fake_quant=True) transposed columns
+          dequantize(q, scale, axis=1), fake_quant(x, axis=1)
+          quantize_rowwise_grouped([x0, x1, ...])              one launch
+          e8m0_to_fp32(scale)                                  fp32 scale view
+  MXFP4   mxfp4_quantize(x, fake_quant=False), mxfp4_dequantize(q, s),
+          mxfp4_simulate_qat(x)
+  FP8     blockfp8_quantize(x, blk=128) / blockfp8_dequantize(q, S, blk=128),
+          blockfp8_quantize_gkn / blockfp8_dequantize_gkn      [G, K, N] stacks
+          blockfp8_quantize_1x128 / blockfp8_dequantize_1x128 / fp8_simulate_qat
+          blockfp8_to_mxfp8(q, S)                              FP8 -> BF16 -> MXFP8
+  NVFP4   nvfp4_quantize(x) / nvfp4_dequantize(q, s, g),
+          nvfp4_quantize_grouped(xs, groups, n_groups)         shared global scales
 and the adapter-level helpers of the MXFP8 export path ("PR #1935 完整报告",
 实现拆解 item 1 and 关键源码片段):
   mxfp8_quantize(weight) -> (qweight, scale)     flattens leading dims to 2-D
