@@ -18,12 +18,15 @@ def check_mxfp4(gpu, orc, x_bits, name):
     announce(f"mxfp4 {name} {x_bits.shape}")
     x = to_dev_bf16(x_bits)
     q, s, fq = gpu.mxfp4_quantize(x, fake_quant=True)
+    q_only, s_only = gpu.mxfp4_quantize(x)          # the quantize-only launch (own tile order)
     only = gpu.mxfp4_simulate_qat(x)
     torch.cuda.synchronize()
     oq, os_ = orc.mxfp4_quantize(x_bits)
     ofq = orc.mxfp4_dequantize(oq, os_)
     assert_same(f"{name} q", u8(q), oq)
     assert_same(f"{name} scale", u8(s), os_)
+    assert_same(f"{name} q (quantize only)", u8(q_only), oq)
+    assert_same(f"{name} scale (quantize only)", u8(s_only), os_)
     assert_same(f"{name} fq", bits16(fq), ofq)
     assert_same(f"{name} fake-quant only", bits16(only), ofq)
     dq = gpu.mxfp4_dequantize(q, s)
