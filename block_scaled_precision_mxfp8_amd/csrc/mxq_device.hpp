@@ -172,20 +172,8 @@ __device__ __forceinline__ uint32_t signs4(uint32_t w0, uint32_t w1)
     return __builtin_amdgcn_perm(w1, w0, 0x07050301u) & 0x80808080u;
 }
 
-// 4 E4M3 codes (bytes 0..3 <- elements 0..3 of (w0, w1)), with one ldexp
-// exponent e = 7 - s for all four (a row group).  NaN group -> 0x7F | sign.
-__device__ __forceinline__ uint32_t e4m3x4_row(uint32_t w0, uint32_t w1, int e, bool nan_group)
-{
-    uint32_t c0 = e4m3_mag_bf16hi(w0 << 16, e);
-    uint32_t c1 = e4m3_mag_bf16hi(w0 & 0xFFFF0000u, e);
-    uint32_t c2 = e4m3_mag_bf16hi(w1 << 16, e);
-    uint32_t c3 = e4m3_mag_bf16hi(w1 & 0xFFFF0000u, e);
-    uint32_t mags = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    mags = nan_group ? 0x7F7F7F7Fu : mags;
-    return mags | signs4(w0, w1);
-}
-
-// Same with a separate exponent / NaN flag per element (column groups).
+// 4 E4M3 codes (bytes 0..3 <- elements 0..3 of (w0, w1)) in software, with a
+// separate ldexp exponent e = 7 - s and NaN flag per element (column groups).
 __device__ __forceinline__ uint32_t e4m3x4_col(uint32_t w0, uint32_t w1, int e0, int e1, int e2,
                                                int e3, bool n0, bool n1, bool n2, bool n3)
 {
