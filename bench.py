@@ -87,9 +87,10 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this quantizer has no cross-GPU step "
-              f"(--gpus {args.gpus}, WORLD_SIZE {world} requested); run with --gpus 1",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} "
+              f"requested): the quantizers run per GPU shard with no exchange except NVFP4's "
+              f"4-byte global-amax MAX, which this single-GPU build does not implement; "
+              f"run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
