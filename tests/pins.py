@@ -382,6 +382,16 @@ def torch_blockfp8(x: np.ndarray, blk: int, bc: int | None = None):
     return q, S.numpy()
 
 
+def pin_mx_fake_quant(orc, x):
+    """Fake quantization equals the dequantization of the quantization along
+    the same axis (row groups with row scales, column groups with column
+    scales), composed here from the separately pinned steps."""
+    for axis in (0, 1):
+        fq = orc.mxfp8_fake_quant(x, axis)
+        q, s = orc.mxfp8_quantize_rowwise(x) if axis == 1 else orc.mxfp8_quantize_colwise(x)
+        assert np.array_equal(fq, orc.mxfp8_dequantize(q, s, axis)), axis
+
+
 def pin_blockfp8_1x128(orc, x):
     """1 x 128 activation blocks: torch composition, the row-group max maps to
     0x7E, dequantization via torch products, fake quant = dequant(quant)."""

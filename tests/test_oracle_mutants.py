@@ -68,6 +68,14 @@ MUTANTS = [
     ("e2m1 saturates at 4", "if (r > 6.0) return sign | 0x7;", "if (r > 4.0) return sign | 0x6;"),
     ("e2m1 quantum", "if (E < 0) E = 0; ", "if (E < -1) E = -1; "),
     ("dequant NaN sign", "o = (uint16_t)((code & 0x80) ? 0xFFC0 : 0x7FC0);", "o = (uint16_t)0x7FC0;"),
+    ("fake-quant axis 0 dequantizes along rows", "orc_mxfp8_dequantize(q, s, rows, cols, axis, out);",
+     "orc_mxfp8_dequantize(q, s, rows, cols, 1, out);"),
+    ("1x128 fake-quant dequantizes with 128x128 tile scales",
+     "orc_blockfp8_dequantize_rect(q, S, rows, cols, 1, 128, out);",
+     "orc_blockfp8_dequantize_rect(q, S, rows, cols, 128, 128, out);"),
+    ("grouped NVFP4 encodes with group 0's scale",
+     "nv_quantize_given(xs[i], rows[i], cols[i], gs[group[i]], nf[group[i]], qs[i], ss[i]);",
+     "nv_quantize_given(xs[i], rows[i], cols[i], gs[0], nf[0], qs[i], ss[i]);"),
 ]
 
 
@@ -91,6 +99,7 @@ def all_pins(orc):
     pins.pin_mx_colwise_t_is_rowwise_of_transpose(orc, workloads.random_bf16((70, 96), 18))
     pins.pin_mx_dequant_vs_torch(orc)
     pins.pin_mx_roundtrip(orc, workloads.mx_small())
+    pins.pin_mx_fake_quant(orc, workloads.random_bf16((70, 96), 19))
     pins.pin_blockfp8(orc, workloads.random_bf16((200, 300), 19), 128)
     z = workloads.random_bf16((128, 256), 20)
     z[:, :128] = 0
