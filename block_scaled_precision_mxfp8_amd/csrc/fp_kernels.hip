@@ -1,5 +1,9 @@
-// fp_kernels.hip -- block-FP8 (128 x 128 absmax, fp32 scale) and NVFP4
-// (global fp32 scale x per-16 E4M3 scale, E2M1 elements) for gfx950.
+// fp_kernels.hip -- block-FP8 and NVFP4 for gfx950: block-FP8 over 128 x 128
+// tiles (also per slice of a [G, K, N] stack) and over 1 x 128 activation
+// blocks with their fake quantization, the FP8 block -> BF16 -> MXFP8
+// re-quantization in one pass, NVFP4 (global fp32 scale x per-16 E4M3 scale,
+// E2M1 elements) single-tensor and grouped with shared global scales, and the
+// dequantizers.
 //
 // Method (xorl PR #30 "Add FP8, NVFP4, and QARL training and export", deep
 // review, "What looked solid"): block-FP8 absmax scaling; NVFP4 two-level
@@ -8,8 +12,9 @@
 // FP4 output packed two per byte, [..., N/2] (miles PR #1372 "V4 mxfp4",
 // review of fp4_act_quant).  The steps the method defines in fp32 -- the
 // scale divisions, the element quotients and the dequantization products --
-// are single IEEE fp32 operations here, correctly rounded (HIP's default
-// fp32 division; no fast-math, denormals kept).
+// give the correctly rounded fp32 result: an IEEE division, or a reciprocal
+// with one FMA correction where that is proven to give the same quotient
+// (div_markstein); no fast-math, denormals kept.
 #include <math.h>
 
 #include "launch.hpp"
