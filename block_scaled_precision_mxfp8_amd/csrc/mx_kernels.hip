@@ -1,6 +1,7 @@
 // mx_kernels.hip -- MXFP8 kernels for gfx950: row-wise quantize (+ fused
-// fake-quant), one-pass column-wise + row-wise + fake-quant, dequantize, and
-// the grouped row-wise launch over many tensors.
+// fake-quant), one-pass column-wise + row-wise + fake-quant (columns in x's
+// layout or transposed), dequantize, the E8M0 -> fp32 scale view, and the
+// grouped row-wise launch over many tensors.
 //
 // Method ("PR #1935 完整报告 / Use TransformerEngine for MXFP8 quantization",
 // section 实现拆解 item 1): groups of 32 consecutive values share one
@@ -15,7 +16,8 @@
 // steps; a column group of 32 is 32 rows of the same lane, so its amax stays
 // in the lane.  All of this is HBM streaming: there is no reuse across
 // workgroups, so the blockIdx -> tile order only keeps each workgroup's
-// accesses contiguous.
+// accesses contiguous, except where workgroups share a scale line (the
+// transposed column-only launch groups those on one XCD).
 #include "launch.hpp"
 #include "mxq_device.hpp"
 
