@@ -30,6 +30,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -50,10 +51,15 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are dropped,
+    so a comment edit does not invalidate counters taken on the same code."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
