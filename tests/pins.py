@@ -271,6 +271,30 @@ def pin_mx_edge_groups(orc, x=None):
     assert np.array_equal(q.astype(np.int64), ref)
 
 
+def mx_saturation_group():
+    """The hand-derived saturation group of tests/golden/mx_saturation_group.txt:
+    (x bits [1, 32], expected scale byte, expected codes [32])."""
+    x = np.zeros((1, 32), np.uint16)
+    codes = np.zeros(32, np.int64)
+    scale = None
+    for parts in read_golden("mx_saturation_group.txt"):
+        if parts[0] == "scale":
+            scale = int(parts[1], 16)
+        else:
+            i, bits, code = int(parts[0]), int(parts[1], 16), int(parts[2], 16)
+            x[0, i], codes[i] = bits, code
+    return x, scale, codes
+
+
+def pin_mx_saturation(orc):
+    """Values at and above E4M3's largest finite 448 saturate to 0x7E with their
+    sign (hand-derived golden group)."""
+    x, scale, codes = mx_saturation_group()
+    q, s = orc.mxfp8_quantize_rowwise(x)
+    assert int(s[0, 0]) == scale
+    assert np.array_equal(q[0].astype(np.int64), codes)
+
+
 def pin_mx_max_code_band(orc, x):
     """Power-of-two scale with exponent floor(log2 amax) - 8: the group max maps
     into [256, 512) before rounding, so its code lies in 0x78..0x7E whenever the

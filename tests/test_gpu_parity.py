@@ -67,7 +67,11 @@ def test_rowwise_nonfinite_zero_subnormal(gpu, orc):
     x[6, 100] = 0x7F7F                               # max finite bf16 (scale byte 246)
     x[7, 0:32] = 0x0001                              # min subnormal
     x[8, 0:32] = rng.integers(0, 0x10000, 32).astype(np.uint16) & 0x7FFF | 0x8000
-    check_rowwise(gpu, orc, x, "edge")
+    sat, sat_scale, sat_codes = pins.mx_saturation_group()  # 500, 480, 464, 460 -> 0x7E
+    x[9, 0:32] = sat[0]
+    q, s = check_rowwise(gpu, orc, x, "edge")
+    assert int(u8(s)[9, 0]) == sat_scale
+    assert np.array_equal(u8(q)[9, 0:32].astype(np.int64), sat_codes)
 
 
 @pytest.mark.parametrize("rows", [1, 31, 33, 97])

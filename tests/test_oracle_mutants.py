@@ -92,6 +92,7 @@ def all_pins(orc):
     pins.pin_mx_sweep(orc, scale_bytes=list(range(0, 24)) + list(range(24, 247, 11)))
     pins.pin_mx_nonfinite(orc)
     pins.pin_mx_edge_groups(orc)
+    pins.pin_mx_saturation(orc)
     x = workloads.random_bf16((97, 256), 17)
     pins.pin_mx_max_code_band(orc, x)
     pins.pin_mx_padcrop(orc, x)

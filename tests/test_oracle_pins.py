@@ -19,6 +19,10 @@ def test_e8m0_decode(orc):
     pins.pin_e8m0_decode(orc)
 
 
+def test_mx_saturation_golden(orc):
+    pins.pin_mx_saturation(orc)
+
+
 def test_e8m0_to_fp32_matches_torch_cast(orc):
     """The fp32 scale view against torch's float8_e8m0fnu -> float32 cast, all
     256 bytes (NaN for 0xFF, the subnormal 2^-127 for 0)."""
