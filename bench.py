@@ -19,7 +19,7 @@ Besides the timed steps it reports, in the same line:
                 from the committed rocprofv3 counter summary when it still
                 matches the kernel source
   cpu_baseline  the CPU oracle (single-threaded C) timed on a bounded sample
-                of the same workload
+                of the same workload, and the same sharded over host threads
   breakdown     every other quantizer workload (row-wise weight, grouped MoE
                 experts, block-FP8, NVFP4, dequantizers), each timed on its own
 """
@@ -238,6 +238,28 @@ def main():
                "sample": f"{args.cpu_rows} of {rows} rows of the same batch: row-wise + "
                          f"column-wise quantize and row-wise dequantize (the step's outputs), "
                          f"{dt:.1f} s single-threaded"}
+        # the same oracle calls sharded by 32-row ranges over host threads (the
+        # C calls release the GIL), for context next to the single-core figure
+        import threading
+        nthreads = max(1, min(16, os.cpu_count() or 1))
+        chunk = ((args.cpu_rows + nthreads - 1) // nthreads + 31) // 32 * 32
+        ranges = [(r, min(r + chunk, args.cpu_rows)) for r in range(0, args.cpu_rows, chunk)]
+
+        def shard(r0, r1):
+            xs = np.ascontiguousarray(sample[r0:r1])
+            sq, ss = orc.mxfp8_quantize_rowwise(xs)
+            orc.mxfp8_quantize_colwise(xs)
+            orc.mxfp8_dequantize(sq, ss, 1)
+
+        workers = [threading.Thread(target=shard, args=rg) for rg in ranges]
+        t = time.perf_counter()
+        for w in workers:
+            w.start()
+        for w in workers:
+            w.join()
+        dt_mt = time.perf_counter() - t
+        cpu["all_threads"] = {"value": round(sbytes / dt_mt / 1e9, 4), "unit": "GB/s",
+                              "cores": len(ranges), "seconds": round(dt_mt, 2)}
 
     # ------------------------------------------------------------------
     # breakdown: every other workload, timed on its own
