@@ -235,6 +235,36 @@ def test_colwise_output_alignment_with_guard_bands(gpu, orc, offset):
                 orc.mxfp8_dequantize(oqr, osr, 1))
 
 
+def test_act_16384_rowwise_dequant_fakequant_full(gpu, orc):
+    """The [16384, 7168] activation through the bench's other single-tensor
+    launches, every output byte: row-wise quantize with fused fake-quant,
+    fake-quant alone on both axes, dequantize on both axes."""
+    xb = workloads.act_16384()
+    announce("act_16384 row-wise + fake-quant")
+    x = to_dev_bf16(xb)
+    q, s, fq = gpu.quantize_rowwise(x, fake_quant=True)
+    col = gpu.quantize_colwise(x, rowwise=False, fake_quant=False)
+    torch.cuda.synchronize()
+    oq, os_ = orc.mxfp8_quantize_rowwise(xb)
+    oqc, osc = orc.mxfp8_quantize_colwise(xb)
+    ofq_r = orc.mxfp8_dequantize(oq, os_, 1)
+    ofq_c = orc.mxfp8_dequantize(oqc, osc, 0)
+    assert_same("act row q", u8(q), oq)
+    assert_same("act row s", u8(s), os_)
+    assert_same("act row fq", bits16(fq), ofq_r)
+    assert_same("act col q", u8(col["q_col"]), oqc)
+    assert_same("act col s", u8(col["s_col"]), osc)
+    del fq
+    announce("act_16384 dequantize and fake-quant, both axes")
+    for axis, qq, ss, want in ((1, q, s, ofq_r), (0, col["q_col"], col["s_col"], ofq_c)):
+        dq = gpu.dequantize(qq, ss, axis=axis)
+        fqa = gpu.fake_quant(x, axis=axis)
+        torch.cuda.synchronize()
+        assert_same(f"act dequant axis {axis}", bits16(dq), want)
+        assert_same(f"act fake-quant axis {axis}", bits16(fqa), want)
+        del dq, fqa
+
+
 def test_colwise_act_16384_full(gpu, orc):
     """The [16384, 7168] activation: column-wise, row-wise and fake-quant in
     one pass, every output byte, in the launch configuration the bench times."""
