@@ -11,6 +11,7 @@ Entry points (names follow the C ABI):
           quantize_colwise_t(x, rowwise=True, fake_quant=True) transposed columns
           dequantize(q, scale, axis=1), fake_quant(x, axis=1)
           quantize_rowwise_grouped([x0, x1, ...])              one launch
+          prepare_rowwise_grouped(xs).run()                    table built once
           e8m0_to_fp32(scale)                                  fp32 scale view
   MXFP4   mxfp4_quantize(x, fake_quant=False), mxfp4_dequantize(q, s),
           mxfp4_simulate_qat(x)
@@ -20,6 +21,7 @@ Entry points (names follow the C ABI):
           blockfp8_to_mxfp8(q, S)                              FP8 -> BF16 -> MXFP8
   NVFP4   nvfp4_quantize(x) / nvfp4_dequantize(q, s, g),
           nvfp4_quantize_grouped(xs, groups, n_groups)         shared global scales
+          prepare_nvfp4_grouped(xs, groups, n_groups).run()    table built once
 and the adapter-level helpers of the MXFP8 export path ("PR #1935 完整报告",
 实现拆解 item 1 and 关键源码片段):
   mxfp8_quantize(weight) -> (qweight, scale)     flattens leading dims to 2-D
@@ -74,6 +76,10 @@ SIGNATURES = {
     "nvfp4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "nvfp4_grouped_workspace_size": (_sz, [_vp, _i32]),
     "nvfp4_quantize_grouped": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "mxq_grouped_plan_build": (ctypes.c_int, [_vp, _i32, _vp, _vp, _sz]),
+    "mxq_quantize_rowwise_grouped_plan": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "nvfp4_grouped_plan_build": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _sz]),
+    "nvfp4_quantize_grouped_plan": (ctypes.c_int, [_vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -87,6 +93,13 @@ class NvGroupDesc(ctypes.Structure):
     """nvfp4_group_desc."""
     _fields_ = [("x", _vp), ("q", _vp), ("s", _vp), ("rows", _i64), ("cols", _i64),
                 ("scale_group", _i32), ("reserved", _i32)]
+
+
+class GroupedPlan(ctypes.Structure):
+    """mxq_grouped_plan."""
+    _fields_ = [("kind", _i32), ("n_entries", _i32), ("n_groups", _i32), ("reserved", _i32),
+                ("total_tiles", _i64), ("table_bytes", ctypes.c_uint64),
+                ("workspace_bytes", ctypes.c_uint64)]
 
 
 class MXQError(RuntimeError):
@@ -267,12 +280,8 @@ def grouped_workspace(n: int, device) -> torch.Tensor:
     return torch.empty((max(int(nbytes), 16),), dtype=torch.uint8, device=device)
 
 
-def quantize_rowwise_grouped(xs, workspace: torch.Tensor | None = None, outputs=None):
-    """Row-wise MXFP8 of every tensor in xs in one launch.  Returns a list of
-    (q, scale).  ``outputs`` may pass preallocated [(q, scale), ...]."""
+def _mx_group_descs(xs, outputs):
     n = len(xs)
-    if n == 0:
-        return []
     dev = xs[0].device
     if outputs is None:
         outputs = []
@@ -291,12 +300,74 @@ def quantize_rowwise_grouped(xs, workspace: torch.Tensor | None = None, outputs=
             raise ValueError(f"xs[{i}] needs unit column stride")
         descs[i] = GroupDesc(x.data_ptr(), q.data_ptr(), s.data_ptr(), rows, cols,
                              x.stride(0), q.stride(0), s.stride(0))
+    return descs, outputs
+
+
+def quantize_rowwise_grouped(xs, workspace: torch.Tensor | None = None, outputs=None):
+    """Row-wise MXFP8 of every tensor in xs in one launch.  Returns a list of
+    (q, scale).  ``outputs`` may pass preallocated [(q, scale), ...]."""
+    n = len(xs)
+    if n == 0:
+        return []
+    descs, outputs = _mx_group_descs(xs, outputs)
     if workspace is None:
-        workspace = grouped_workspace(n, dev)
+        workspace = grouped_workspace(n, xs[0].device)
     st = load().mxq_quantize_rowwise_grouped(descs, n, _ptr(workspace), workspace.numel(),
                                              _stream(xs[0]))
     _check("mxq_quantize_rowwise_grouped", st)
     return outputs
+
+
+class PreparedGroup:
+    """A grouped launch whose table was built once and copied to the device.
+
+    ``run()`` launches on the current stream and does nothing else (no copy,
+    no allocation), so it can be captured in a HIP graph.  The object keeps the
+    input and output tensors it names alive; refill the inputs in place and
+    call ``run()`` again.  ``outputs`` are the per-tensor results, and
+    ``global_scales`` the NVFP4 group scales (None for MXFP8)."""
+
+    def __init__(self, kind, plan, buf, xs, outputs, global_scales=None):
+        self.kind, self.plan, self.buf = kind, plan, buf
+        self.xs, self.outputs, self.global_scales = xs, outputs, global_scales
+
+    def run(self):
+        sp = ctypes.c_void_p(torch.cuda.current_stream(self.buf.device).cuda_stream)
+        L = load()
+        if self.kind == "mxfp8":
+            st = L.mxq_quantize_rowwise_grouped_plan(ctypes.byref(self.plan), _ptr(self.buf),
+                                                     self.buf.numel(), sp)
+            _check("mxq_quantize_rowwise_grouped_plan", st)
+            return self.outputs
+        st = L.nvfp4_quantize_grouped_plan(ctypes.byref(self.plan), _ptr(self.global_scales),
+                                           _ptr(self.buf), self.buf.numel(), sp)
+        _check("nvfp4_quantize_grouped_plan", st)
+        return self.outputs, self.global_scales
+
+
+def _plan_table(build, args, fn, dev):
+    """Runs a plan build twice (sizes, then the host image) and copies the
+    image to the front of a new device buffer of the plan's workspace size."""
+    plan = GroupedPlan()
+    _check(fn, build(*args, ctypes.byref(plan), None, 0))
+    img = (ctypes.c_ubyte * max(int(plan.table_bytes), 1))()
+    _check(fn, build(*args, ctypes.byref(plan), img, int(plan.table_bytes)))
+    buf = torch.empty((max(int(plan.workspace_bytes), 16),), dtype=torch.uint8, device=dev)
+    if plan.table_bytes:
+        host = torch.frombuffer(bytearray(img), dtype=torch.uint8)[: int(plan.table_bytes)]
+        buf[: int(plan.table_bytes)].copy_(host)
+    return plan, buf
+
+
+def prepare_rowwise_grouped(xs, outputs=None) -> PreparedGroup:
+    """Row-wise MXFP8 of xs as quantize_rowwise_grouped, prepared once."""
+    if len(xs) == 0:
+        raise ValueError("no tensors")
+    descs, outputs = _mx_group_descs(xs, outputs)
+    L = load()
+    plan, buf = _plan_table(L.mxq_grouped_plan_build, (descs, len(xs)),
+                            "mxq_grouped_plan_build", xs[0].device)
+    return PreparedGroup("mxfp8", plan, buf, list(xs), outputs)
 
 
 # ---------------------------------------------------------------------------
@@ -472,23 +543,18 @@ def nvfp4_quantize(x: torch.Tensor, workspace: torch.Tensor | None = None):
     return q, s, g
 
 
-def nvfp4_quantize_grouped(xs, groups, n_groups: int, workspace: torch.Tensor | None = None):
-    """NVFP4 of every 2-D bf16 tensor in xs in one call, the global scale shared
-    within scale groups (groups[i] is tensor i's group).  Returns
-    ([(q, s), ...], g float32 [n_groups])."""
+def _nv_group_descs(xs, groups, n_groups):
     if len(xs) != len(groups):
         raise ValueError("one scale group per tensor")
     if n_groups < 1:
         raise ValueError("n_groups must be >= 1")
-    dev = None
+    if len(xs) == 0:
+        raise ValueError("no tensors")
     for x in xs:
         _need_bf16_cuda(x)
         if x.dim() != 2:
             raise ValueError("nvfp4_quantize_grouped expects 2-D tensors")
-        dev = x.device
-    xs = [x.contiguous() for x in xs]
-    if dev is None:
-        raise ValueError("no tensors")
+    dev = xs[0].device
     outs = [(torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev),
              torch.empty((x.shape[0], x.shape[1] // NV_BLOCK), dtype=torch.uint8, device=dev))
             for x in xs]
@@ -499,14 +565,36 @@ def nvfp4_quantize_grouped(xs, groups, n_groups: int, workspace: torch.Tensor | 
         descs[i] = NvGroupDesc(None if empty else x.data_ptr(), None if empty else q.data_ptr(),
                                None if empty else s.data_ptr(), x.shape[0], x.shape[1],
                                int(groups[i]), 0)
+    return descs, outs, gs
+
+
+def nvfp4_quantize_grouped(xs, groups, n_groups: int, workspace: torch.Tensor | None = None):
+    """NVFP4 of every 2-D bf16 tensor in xs in one call, the global scale shared
+    within scale groups (groups[i] is tensor i's group).  Returns
+    ([(q, s), ...], g float32 [n_groups])."""
+    xs = [x.contiguous() for x in xs]
+    descs, outs, gs = _nv_group_descs(xs, groups, n_groups)
     L = load()
     nbytes = L.nvfp4_grouped_workspace_size(descs, len(xs))
     if workspace is None:
-        workspace = torch.empty((max(int(nbytes), 16),), dtype=torch.uint8, device=dev)
+        workspace = torch.empty((max(int(nbytes), 16),), dtype=torch.uint8, device=xs[0].device)
     st = L.nvfp4_quantize_grouped(descs, len(xs), _ptr(gs), n_groups, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(xs[0]))
     _check("nvfp4_quantize_grouped", st)
     return outs, gs
+
+
+def prepare_nvfp4_grouped(xs, groups, n_groups: int) -> PreparedGroup:
+    """nvfp4_quantize_grouped prepared once; xs must be contiguous (they are
+    read in place at every run)."""
+    for i, x in enumerate(xs):
+        if not x.is_contiguous():
+            raise ValueError(f"xs[{i}] must be contiguous")
+    descs, outs, gs = _nv_group_descs(xs, groups, n_groups)
+    L = load()
+    plan, buf = _plan_table(L.nvfp4_grouped_plan_build, (descs, len(xs), int(n_groups)),
+                            "nvfp4_grouped_plan_build", xs[0].device)
+    return PreparedGroup("nvfp4", plan, buf, list(xs), outs, gs)
 
 
 def nvfp4_dequantize(q: torch.Tensor, s: torch.Tensor, g: torch.Tensor) -> torch.Tensor:

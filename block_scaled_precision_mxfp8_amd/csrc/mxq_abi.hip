@@ -55,6 +55,165 @@ mxq_status check_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t 
     return MXQ_OK;
 }
 
+size_t round16(size_t v) { return (v + 15) / 16 * 16; }
+
+// Launch tables of the grouped calls, as one host image copied to the front
+// of the device buffer:
+//   MXFP8  [GroupEntry x m][int32 first tile x m]
+//   NVFP4  [NvEntry x m][int32 first tile x m][int32 scale group x m],
+//          followed in the buffer by one uint32 amax partial per tile
+// each padded to 16 bytes, m = the non-empty descriptors.
+constexpr int32_t kPlanMx = 0x3158584D;  // "MXX1"
+constexpr int32_t kPlanNv = 0x3134564E;  // "NV41"
+
+size_t mx_table_bytes(size_t m) { return round16(m * (sizeof(GroupEntry) + sizeof(int32_t))); }
+
+size_t nv_table_bytes(size_t m)
+{
+    return round16(m * (sizeof(mxq::NvEntry) + 2 * sizeof(int32_t)));
+}
+
+template <class T>
+void put(std::vector<unsigned char> &img, size_t off, const std::vector<T> &v)
+{
+    if (!v.empty()) memcpy(img.data() + off, v.data(), v.size() * sizeof(T));
+}
+
+// Checks descs as mxq_quantize_rowwise does and builds the MXFP8 table image.
+mxq_status mx_build(const mxq_group_desc *descs, int32_t n, std::vector<unsigned char> &img,
+                    mxq_grouped_plan &plan)
+{
+    if (n < 0 || (n > 0 && !descs)) return MXQ_EINVAL;
+    std::vector<GroupEntry> table;
+    std::vector<int32_t> starts;
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const mxq_group_desc &d = descs[i];
+        mxq_status st = check_rowwise(d.x, d.rows, d.cols, d.ldx, d.q, d.ldq, d.scale, d.lds,
+                                      nullptr, 0, true);
+        if (st != MXQ_OK) return st;
+        if (d.rows == 0 || d.cols == 0) continue;
+        GroupEntry e;
+        e.x = d.x;
+        e.q = d.q;
+        e.scale = d.scale;
+        e.rows = d.rows;
+        e.cols = d.cols;
+        e.ldx = d.ldx;
+        e.ldq = d.ldq;
+        e.lds = d.lds;
+        e.tile_begin = tiles;
+        const int64_t t = mxq::mx_row_tiles(d.rows, d.cols, &e.nseg);
+        if (__builtin_add_overflow(tiles, t, &tiles) || tiles > 0x7FFFFFFF) return MXQ_ESIZE;
+        table.push_back(e);
+        starts.push_back((int32_t)e.tile_begin);
+    }
+    const size_t m = table.size();
+    img.assign(mx_table_bytes(m), 0);
+    put(img, 0, table);
+    put(img, m * sizeof(GroupEntry), starts);
+    plan = mxq_grouped_plan{};
+    plan.kind = kPlanMx;
+    plan.n_entries = (int32_t)m;
+    plan.total_tiles = tiles;
+    plan.table_bytes = img.size();
+    plan.workspace_bytes = img.size();
+    return MXQ_OK;
+}
+
+// Checks descs as nvfp4_quantize_grouped does and builds the NVFP4 table image.
+mxq_status nv_build(const nvfp4_group_desc *descs, int32_t n, int32_t n_groups,
+                    std::vector<unsigned char> &img, mxq_grouped_plan &plan)
+{
+    if (n < 0 || n_groups < 0) return MXQ_EINVAL;
+    if (n > 0 && (!descs || n_groups == 0)) return MXQ_EINVAL;
+    std::vector<mxq::NvEntry> table;
+    std::vector<int32_t> starts, groups;
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const nvfp4_group_desc &d = descs[i];
+        if (d.rows < 0 || d.cols < 0 || d.scale_group < 0 || d.scale_group >= n_groups)
+            return MXQ_EINVAL;
+        if (d.cols % 16 != 0) return MXQ_ESHAPE;
+        if (d.rows == 0 || d.cols == 0) continue;
+        if (!d.x || !d.q || !d.s) return MXQ_EINVAL;
+        if (!aligned(d.x, 16) || !aligned(d.q, 4)) return MXQ_EALIGN;
+        if (!fits(d.rows, d.cols)) return MXQ_ESIZE;
+        mxq::NvEntry e;
+        e.x = d.x;
+        e.q = d.q;
+        e.s = d.s;
+        e.rows = d.rows;
+        e.cols = d.cols;
+        const int64_t t = mxq::nvfp4_tiles(d.rows, d.cols, &e.nseg);
+        e.tile_begin = (int32_t)tiles;
+        e.group = d.scale_group;
+        if (__builtin_add_overflow(tiles, t, &tiles) || tiles > 0x7FFFFFFF) return MXQ_ESIZE;
+        table.push_back(e);
+        starts.push_back(e.tile_begin);
+        groups.push_back(e.group);
+    }
+    const size_t m = table.size();
+    img.assign(nv_table_bytes(m), 0);
+    put(img, 0, table);
+    put(img, m * sizeof(mxq::NvEntry), starts);
+    put(img, m * (sizeof(mxq::NvEntry) + sizeof(int32_t)), groups);
+    plan = mxq_grouped_plan{};
+    plan.kind = kPlanNv;
+    plan.n_entries = (int32_t)m;
+    plan.n_groups = n_groups;
+    plan.total_tiles = tiles;
+    plan.table_bytes = img.size();
+    plan.workspace_bytes = img.size() + round16((size_t)tiles * sizeof(uint32_t));
+    return MXQ_OK;
+}
+
+// A plan as the build call of its kind leaves it.
+bool plan_ok(const mxq_grouped_plan *p, int32_t kind)
+{
+    if (!p || p->kind != kind || p->n_entries < 0 || p->reserved != 0) return false;
+    if (p->total_tiles < 0 || p->total_tiles > 0x7FFFFFFF) return false;
+    if ((p->n_entries == 0) != (p->total_tiles == 0)) return false;
+    if (kind == kPlanMx)
+        return p->n_groups == 0 && p->table_bytes == mx_table_bytes((size_t)p->n_entries) &&
+               p->workspace_bytes == p->table_bytes;
+    return p->n_groups >= 0 && (p->n_entries == 0 || p->n_groups > 0) &&
+           p->table_bytes == nv_table_bytes((size_t)p->n_entries) &&
+           p->workspace_bytes ==
+               p->table_bytes + round16((size_t)p->total_tiles * sizeof(uint32_t));
+}
+
+mxq_status launch_mx_plan(const mxq_grouped_plan &p, const void *table, hipStream_t stream)
+{
+    const unsigned char *t = static_cast<const unsigned char *>(table);
+    return from_hip(mxq::launch_mx_grouped(
+        reinterpret_cast<const GroupEntry *>(t),
+        reinterpret_cast<const int32_t *>(t + (size_t)p.n_entries * sizeof(GroupEntry)),
+        p.n_entries, p.total_tiles, stream));
+}
+
+mxq_status launch_nv_plan(const mxq_grouped_plan &p, float *gs, void *workspace,
+                          hipStream_t stream)
+{
+    unsigned char *w = static_cast<unsigned char *>(workspace);
+    const size_t m = (size_t)p.n_entries;
+    return from_hip(mxq::launch_nvfp4_grouped(
+        reinterpret_cast<const mxq::NvEntry *>(w),
+        reinterpret_cast<const int32_t *>(w + m * sizeof(mxq::NvEntry)),
+        reinterpret_cast<const int32_t *>(w + m * (sizeof(mxq::NvEntry) + sizeof(int32_t))),
+        p.n_entries, reinterpret_cast<uint32_t *>(w + p.table_bytes), p.total_tiles, gs,
+        p.n_groups, stream));
+}
+
+// Writes the image for a build call: NULL table_host only reports the plan.
+mxq_status hand_over(const std::vector<unsigned char> &img, void *table_host, size_t bytes)
+{
+    if (!table_host) return MXQ_OK;
+    if (bytes < img.size()) return MXQ_ESIZE;
+    if (!img.empty()) memcpy(table_host, img.data(), img.size());
+    return MXQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,47 +369,39 @@ mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n, 
     if (!descs || !workspace) return MXQ_EINVAL;
     if (!aligned(workspace, 16)) return MXQ_EALIGN;
     if (workspace_bytes < mxq_grouped_workspace_size(n)) return MXQ_ESIZE;
-    std::vector<GroupEntry> table;
-    std::vector<int32_t> starts;
-    table.reserve((size_t)n);
-    starts.reserve((size_t)n);
-    int64_t tiles = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        const mxq_group_desc &d = descs[i];
-        mxq_status st = check_rowwise(d.x, d.rows, d.cols, d.ldx, d.q, d.ldq, d.scale, d.lds,
-                                      nullptr, 0, true);
-        if (st != MXQ_OK) return st;
-        if (d.rows == 0 || d.cols == 0) continue;
-        GroupEntry e;
-        e.x = d.x;
-        e.q = d.q;
-        e.scale = d.scale;
-        e.rows = d.rows;
-        e.cols = d.cols;
-        e.ldx = d.ldx;
-        e.ldq = d.ldq;
-        e.lds = d.lds;
-        e.tile_begin = tiles;
-        const int64_t t = mxq::mx_row_tiles(d.rows, d.cols, &e.nseg);
-        if (__builtin_add_overflow(tiles, t, &tiles) || tiles > 0x7FFFFFFF) return MXQ_ESIZE;
-        table.push_back(e);
-        starts.push_back((int32_t)e.tile_begin);
-    }
-    if (table.empty()) return MXQ_OK;
-    // One staging buffer: the table, then the first-tile array right after the
-    // n entries the workspace was sized for.  Pageable source: the copy has
-    // consumed it by the time hipMemcpyAsync returns.
-    const size_t tbytes = (size_t)n * sizeof(GroupEntry);
-    std::vector<unsigned char> stage(tbytes + starts.size() * sizeof(int32_t));
-    memcpy(stage.data(), table.data(), table.size() * sizeof(GroupEntry));
-    memcpy(stage.data() + tbytes, starts.data(), starts.size() * sizeof(int32_t));
-    hipError_t err = hipMemcpyAsync(workspace, stage.data(), stage.size(), hipMemcpyHostToDevice,
-                                    as_stream(stream));
-    if (err != hipSuccess) return MXQ_EHIP;
-    unsigned char *ws = static_cast<unsigned char *>(workspace);
-    return from_hip(mxq::launch_mx_grouped(reinterpret_cast<const GroupEntry *>(ws),
-                                           reinterpret_cast<const int32_t *>(ws + tbytes),
-                                           (int32_t)table.size(), tiles, as_stream(stream)));
+    std::vector<unsigned char> img;
+    mxq_grouped_plan plan;
+    mxq_status st = mx_build(descs, n, img, plan);
+    if (st != MXQ_OK || plan.n_entries == 0) return st;
+    // pageable source: the copy has consumed it by the time hipMemcpyAsync returns
+    if (hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice,
+                       as_stream(stream)) != hipSuccess)
+        return MXQ_EHIP;
+    return launch_mx_plan(plan, workspace, as_stream(stream));
+}
+
+mxq_status mxq_grouped_plan_build(const mxq_group_desc *descs, int32_t n, mxq_grouped_plan *plan,
+                                  void *table_host, size_t table_host_bytes)
+{
+    if (!plan) return MXQ_EINVAL;
+    std::vector<unsigned char> img;
+    mxq_grouped_plan p;
+    mxq_status st = mx_build(descs, n, img, p);
+    if (st != MXQ_OK) return st;
+    st = hand_over(img, table_host, table_host_bytes);
+    if (st == MXQ_OK) *plan = p;
+    return st;
+}
+
+mxq_status mxq_quantize_rowwise_grouped_plan(const mxq_grouped_plan *plan, const void *table_dev,
+                                             size_t table_dev_bytes, void *stream)
+{
+    if (!plan_ok(plan, kPlanMx)) return MXQ_EINVAL;
+    if (plan->n_entries == 0) return MXQ_OK;
+    if (!table_dev) return MXQ_EINVAL;
+    if (!aligned(table_dev, 16)) return MXQ_EALIGN;
+    if (table_dev_bytes < plan->workspace_bytes) return MXQ_ESIZE;
+    return launch_mx_plan(*plan, table_dev, as_stream(stream));
 }
 
 mxq_status blockfp8_quantize(const uint16_t *x, int64_t rows, int64_t cols, int32_t blk,
@@ -372,14 +523,6 @@ mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t
                                             static_cast<uint32_t *>(workspace), as_stream(stream)));
 }
 
-namespace {
-size_t round16(size_t v) { return (v + 15) / 16 * 16; }
-size_t nv_table_bytes(int32_t n)
-{
-    return round16((size_t)n * (sizeof(mxq::NvEntry) + 2 * sizeof(int32_t)));
-}
-}  // namespace
-
 size_t nvfp4_grouped_workspace_size(const nvfp4_group_desc *descs, int32_t n)
 {
     if (n <= 0 || !descs) return 0;
@@ -387,7 +530,7 @@ size_t nvfp4_grouped_workspace_size(const nvfp4_group_desc *descs, int32_t n)
     for (int32_t i = 0; i < n; ++i)
         if (descs[i].rows > 0 && descs[i].cols > 0)
             tiles += (size_t)mxq::nvfp4_tiles(descs[i].rows, descs[i].cols, nullptr);
-    return nv_table_bytes(n) + round16(tiles * sizeof(uint32_t));
+    return nv_table_bytes((size_t)n) + round16(tiles * sizeof(uint32_t));
 }
 
 mxq_status nvfp4_quantize_grouped(const nvfp4_group_desc *descs, int32_t n, float *global_scales,
@@ -399,55 +542,47 @@ mxq_status nvfp4_quantize_grouped(const nvfp4_group_desc *descs, int32_t n, floa
     if (n_groups == 0) return MXQ_OK;
     if (!global_scales) return MXQ_EINVAL;
     if (!aligned(global_scales, 4)) return MXQ_EALIGN;
-    std::vector<mxq::NvEntry> table;
-    std::vector<int32_t> starts, groups;
-    int64_t tiles = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        const nvfp4_group_desc &d = descs[i];
-        if (d.rows < 0 || d.cols < 0 || d.scale_group < 0 || d.scale_group >= n_groups)
-            return MXQ_EINVAL;
-        if (d.cols % 16 != 0) return MXQ_ESHAPE;
-        if (d.rows == 0 || d.cols == 0) continue;
-        if (!d.x || !d.q || !d.s) return MXQ_EINVAL;
-        if (!aligned(d.x, 16) || !aligned(d.q, 4)) return MXQ_EALIGN;
-        if (!fits(d.rows, d.cols)) return MXQ_ESIZE;
-        mxq::NvEntry e;
-        e.x = d.x;
-        e.q = d.q;
-        e.s = d.s;
-        e.rows = d.rows;
-        e.cols = d.cols;
-        const int64_t t = mxq::nvfp4_tiles(d.rows, d.cols, &e.nseg);
-        e.tile_begin = (int32_t)tiles;
-        e.group = d.scale_group;
-        if (__builtin_add_overflow(tiles, t, &tiles) || tiles > 0x7FFFFFFF) return MXQ_ESIZE;
-        table.push_back(e);
-        starts.push_back(e.tile_begin);
-        groups.push_back(e.group);
-    }
+    std::vector<unsigned char> img;
+    mxq_grouped_plan plan;
+    mxq_status st = nv_build(descs, n, n_groups, img, plan);
+    if (st != MXQ_OK) return st;
     if (!workspace) return MXQ_EINVAL;
     if (!aligned(workspace, 16)) return MXQ_EALIGN;
     if (workspace_bytes < nvfp4_grouped_workspace_size(descs, n)) return MXQ_ESIZE;
-    // workspace: [entries x n][first tiles x n][groups x n] | partials
-    const size_t m = table.size();
-    unsigned char *ws = static_cast<unsigned char *>(workspace);
-    const size_t tbytes = (size_t)n * sizeof(mxq::NvEntry);
-    std::vector<unsigned char> stage(tbytes + 2 * (size_t)n * sizeof(int32_t), 0);
-    if (m) {
-        memcpy(stage.data(), table.data(), m * sizeof(mxq::NvEntry));
-        memcpy(stage.data() + tbytes, starts.data(), m * sizeof(int32_t));
-        memcpy(stage.data() + tbytes + (size_t)n * sizeof(int32_t), groups.data(),
-               m * sizeof(int32_t));
-        // pageable source: the copy has consumed it by the time it returns
-        if (hipMemcpyAsync(ws, stage.data(), stage.size(), hipMemcpyHostToDevice,
-                           as_stream(stream)) != hipSuccess)
-            return MXQ_EHIP;
+    // pageable source: the copy has consumed it by the time it returns
+    if (!img.empty() && hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice,
+                                       as_stream(stream)) != hipSuccess)
+        return MXQ_EHIP;
+    return launch_nv_plan(plan, global_scales, workspace, as_stream(stream));
+}
+
+mxq_status nvfp4_grouped_plan_build(const nvfp4_group_desc *descs, int32_t n, int32_t n_groups,
+                                    mxq_grouped_plan *plan, void *table_host,
+                                    size_t table_host_bytes)
+{
+    if (!plan) return MXQ_EINVAL;
+    std::vector<unsigned char> img;
+    mxq_grouped_plan p;
+    mxq_status st = nv_build(descs, n, n_groups, img, p);
+    if (st != MXQ_OK) return st;
+    st = hand_over(img, table_host, table_host_bytes);
+    if (st == MXQ_OK) *plan = p;
+    return st;
+}
+
+mxq_status nvfp4_quantize_grouped_plan(const mxq_grouped_plan *plan, float *global_scales,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!plan_ok(plan, kPlanNv)) return MXQ_EINVAL;
+    if (plan->n_groups == 0) return MXQ_OK;
+    if (!global_scales) return MXQ_EINVAL;
+    if (!aligned(global_scales, 4)) return MXQ_EALIGN;
+    if (plan->workspace_bytes > 0) {  // else no member has elements: only the scales are written
+        if (!workspace) return MXQ_EINVAL;
+        if (!aligned(workspace, 16)) return MXQ_EALIGN;
+        if (workspace_bytes < plan->workspace_bytes) return MXQ_ESIZE;
     }
-    return from_hip(mxq::launch_nvfp4_grouped(
-        reinterpret_cast<const mxq::NvEntry *>(ws), reinterpret_cast<const int32_t *>(ws + tbytes),
-        reinterpret_cast<const int32_t *>(ws + tbytes + (size_t)n * sizeof(int32_t)), (int32_t)m,
-        reinterpret_cast<uint32_t *>(ws + nv_table_bytes(n)), tiles, global_scales, n_groups,
-        as_stream(stream)));
+    return launch_nv_plan(*plan, global_scales, workspace, as_stream(stream));
 }
 
 mxq_status nvfp4_dequantize(const uint8_t *q_packed, const uint8_t *s_e4m3,

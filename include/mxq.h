@@ -352,6 +352,62 @@ mxq_status nvfp4_quantize_grouped(const nvfp4_group_desc *descs, int32_t n, floa
                                   int32_t n_groups, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/*
+ * Grouped launches prepared once.  Both grouped calls above rebuild their
+ * launch table on the host and copy it to the device on every call.  A caller
+ * that quantizes the same set of buffers every step (the experts of an MoE
+ * layer; work replayed from a captured HIP graph) can instead build the table
+ * once and then launch from it: the launch makes no copy and allocates
+ * nothing, so a graph capture records kernels only.  The results equal the
+ * one-call forms' bit for bit.
+ *   1. mxq_grouped_plan_build / nvfp4_grouped_plan_build with table_host ==
+ *      NULL check the descriptors exactly as the one-call form does and fill
+ *      *plan, sizes included.
+ *   2. Called again with plan->table_bytes of host memory at table_host, they
+ *      write the table image there.  The image holds the descriptors' device
+ *      pointers and shapes, so it is valid while those buffers are.
+ *   3. The caller copies the image into the first plan->table_bytes bytes of
+ *      a 16-byte aligned device buffer of >= plan->workspace_bytes bytes.
+ *   4. The *_grouped_plan call launches, as often as wanted.  It checks the
+ *      plan and the buffer's size; the device bytes it trusts to be the image.
+ * A plan of one kind is refused by the other kind's launch (MXQ_EINVAL).
+ * MXFP8 launches only read their buffer; an NVFP4 buffer also holds amax
+ * partials after the image, so NVFP4 launches that overlap on one buffer race.
+ */
+typedef struct mxq_grouped_plan {
+    int32_t kind;             /* written by the build call, checked by the launch */
+    int32_t n_entries;        /* descriptors with rows > 0 and cols > 0 */
+    int32_t n_groups;         /* NVFP4 scale groups (global_scales length); 0 for MXFP8 */
+    int32_t reserved;         /* 0 */
+    int64_t total_tiles;      /* workgroups of the quantize kernel */
+    uint64_t table_bytes;     /* size of the table image */
+    uint64_t workspace_bytes; /* device buffer size the launch needs, image first */
+} mxq_grouped_plan;
+
+/* Errors as mxq_quantize_rowwise_grouped, plus MXQ_EINVAL for plan == NULL
+ * and MXQ_ESIZE for table_host_bytes < plan->table_bytes.  n == 0 gives an
+ * empty plan whose launch does nothing. */
+mxq_status mxq_grouped_plan_build(const mxq_group_desc *descs, int32_t n, mxq_grouped_plan *plan,
+                                  void *table_host, size_t table_host_bytes);
+
+/* table_dev: the device copy of the image.  MXQ_EINVAL for a NULL or foreign
+ * plan, MXQ_EALIGN / MXQ_ESIZE for the buffer. */
+mxq_status mxq_quantize_rowwise_grouped_plan(const mxq_grouped_plan *plan, const void *table_dev,
+                                             size_t table_dev_bytes, void *stream);
+
+/* Errors as nvfp4_quantize_grouped (the workspace checks move to the launch),
+ * plus those of mxq_grouped_plan_build. */
+mxq_status nvfp4_grouped_plan_build(const nvfp4_group_desc *descs, int32_t n, int32_t n_groups,
+                                    mxq_grouped_plan *plan, void *table_host,
+                                    size_t table_host_bytes);
+
+/* workspace: the image, then room for the amax partials
+ * (plan->workspace_bytes in all; may be NULL when that is 0);
+ * global_scales: plan->n_groups floats, 4-byte aligned, written as by
+ * nvfp4_quantize_grouped. */
+mxq_status nvfp4_quantize_grouped_plan(const mxq_grouped_plan *plan, float *global_scales,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* NVFP4 dequantization: out = bf16_RNE(fl32(E2M1(q) * eff)),
  * eff = fl32(E4M3(s) * g); a NaN product gives the quiet NaN with the
  * nibble's sign.  Shapes as nvfp4_quantize; out 16-byte aligned. */

@@ -365,3 +365,84 @@ def test_e8m0_to_fp32_errors(lib):
     assert f(NULL, 8, P16, NULL) == mxq.MXQ_EINVAL
     assert f(P16, 8, NULL, NULL) == mxq.MXQ_EINVAL
     assert f(P16, 8, P2, NULL) == mxq.MXQ_EALIGN
+
+
+def test_grouped_plan_build_and_refusals(lib):
+    """Building a grouped plan runs on the host only: the table image holds
+    every non-empty descriptor with its first tile (tiles are 512-column x
+    32-row blocks, numbered tensor by tensor), and a launch refuses a missing,
+    foreign or altered plan before anything reaches the GPU."""
+    import numpy as np
+    b = lib.mxq_grouped_plan_build
+    descs = (mxq.GroupDesc * 3)()
+    descs[0] = mxq.GroupDesc(0x10000, 0x20000, 0x30000, 40, 1056, 1056, 1056, 33)
+    descs[1] = mxq.GroupDesc(None, None, None, 0, 64, 64, 64, 2)           # empty: no entry
+    descs[2] = mxq.GroupDesc(0x40000, 0x50000, 0x60000, 8, 64, 72, 64, 2)
+    plan = mxq.GroupedPlan()
+    assert b(descs, 3, NULL, NULL, 0) == mxq.MXQ_EINVAL
+    assert b(descs, -1, ctypes.byref(plan), NULL, 0) == mxq.MXQ_EINVAL
+    assert b(NULL, 3, ctypes.byref(plan), NULL, 0) == mxq.MXQ_EINVAL
+    assert b(descs, 3, ctypes.byref(plan), NULL, 0) == mxq.MXQ_OK      # sizes only
+    assert (plan.n_entries, plan.n_groups, plan.total_tiles) == (2, 0, 3 * 2 + 1)
+    assert plan.table_bytes == 176 and plan.workspace_bytes == 176    # 2 x (80 + 4), to 16
+    img = (ctypes.c_ubyte * 176)()
+    assert b(descs, 3, ctypes.byref(plan), img, 175) == mxq.MXQ_ESIZE
+    assert b(descs, 3, ctypes.byref(plan), img, 176) == mxq.MXQ_OK
+    w = np.frombuffer(bytes(img), dtype=np.int64, count=20)
+    assert list(w[:10]) == [0x10000, 0x20000, 0x30000, 40, 1056, 1056, 1056, 33, 0, 3]
+    assert list(w[10:]) == [0x40000, 0x50000, 0x60000, 8, 64, 72, 64, 2, 6, 1]
+    assert list(np.frombuffer(bytes(img), dtype=np.int32, offset=160, count=2)) == [0, 6]
+    bad_desc = (mxq.GroupDesc * 1)(mxq.GroupDesc(0x10000, 0x20000, 0x30000, 8, 48, 48, 48, 2))
+    assert b(bad_desc, 1, ctypes.byref(plan), NULL, 0) == mxq.MXQ_ESHAPE
+    assert plan.n_entries == 2                                         # untouched on error
+    empty = mxq.GroupedPlan()
+    assert b(descs, 0, ctypes.byref(empty), NULL, 0) == mxq.MXQ_OK
+    assert (empty.n_entries, empty.total_tiles, empty.table_bytes) == (0, 0, 0)
+
+    go = lib.mxq_quantize_rowwise_grouped_plan
+    assert go(NULL, P16, 176, NULL) == mxq.MXQ_EINVAL
+    assert go(ctypes.byref(plan), NULL, 176, NULL) == mxq.MXQ_EINVAL
+    assert go(ctypes.byref(plan), P8, 176, NULL) == mxq.MXQ_EALIGN
+    assert go(ctypes.byref(plan), P16, 175, NULL) == mxq.MXQ_ESIZE
+    for field, value in [("kind", 0), ("n_entries", 3), ("reserved", 1), ("total_tiles", -1),
+                         ("table_bytes", 160), ("n_groups", 1)]:
+        alt = mxq.GroupedPlan.from_buffer_copy(plan)
+        setattr(alt, field, value)
+        assert go(ctypes.byref(alt), P16, 176, NULL) == mxq.MXQ_EINVAL, field
+    assert lib.nvfp4_quantize_grouped_plan(ctypes.byref(plan), P16, P16, 176, NULL) == mxq.MXQ_EINVAL
+
+    nb = lib.nvfp4_grouped_plan_build
+    nd = (mxq.NvGroupDesc * 3)()
+    nd[0] = mxq.NvGroupDesc(0x10000, 0x20000, 0x30000, 40, 1056, 1, 0)
+    nd[1] = mxq.NvGroupDesc(None, None, None, 0, 32, 0, 0)
+    nd[2] = mxq.NvGroupDesc(0x40000, 0x50000, 0x60000, 8, 32, 0, 0)
+    nplan = mxq.GroupedPlan()
+    assert nb(nd, 3, 0, ctypes.byref(nplan), NULL, 0) == mxq.MXQ_EINVAL     # no groups
+    assert nb(nd, 3, 1, ctypes.byref(nplan), NULL, 0) == mxq.MXQ_EINVAL     # group 1 out of range
+    assert nb(nd, 3, 2, NULL, NULL, 0) == mxq.MXQ_EINVAL
+    assert nb(nd, 3, 2, ctypes.byref(nplan), NULL, 0) == mxq.MXQ_OK
+    assert (nplan.n_entries, nplan.n_groups, nplan.total_tiles) == (2, 2, 7)
+    assert nplan.table_bytes == 128 and nplan.workspace_bytes == 128 + 32   # 7 partials, to 16
+    nimg = (ctypes.c_ubyte * 128)()
+    assert nb(nd, 3, 2, ctypes.byref(nplan), nimg, 128) == mxq.MXQ_OK
+    raw = bytes(nimg)
+    assert list(np.frombuffer(raw, np.int64, 6, 0)) == [0x10000, 0x20000, 0x30000, 40, 1056, 3]
+    assert list(np.frombuffer(raw, np.int32, 2, 48)) == [0, 1]              # first tile, group
+    assert list(np.frombuffer(raw, np.int64, 6, 56)) == [0x40000, 0x50000, 0x60000, 8, 32, 1]
+    assert list(np.frombuffer(raw, np.int32, 2, 104)) == [6, 0]
+    assert list(np.frombuffer(raw, np.int32, 4, 112)) == [0, 6, 1, 0]       # starts, groups
+    nd[2] = mxq.NvGroupDesc(0x40000, 0x50000, 0x60000, 8, 24, 0, 0)
+    assert nb(nd, 3, 2, ctypes.byref(nplan), NULL, 0) == mxq.MXQ_ESHAPE
+
+    ngo = lib.nvfp4_quantize_grouped_plan
+    assert ngo(ctypes.byref(nplan), NULL, P16, 160, NULL) == mxq.MXQ_EINVAL  # no global scales
+    assert ngo(ctypes.byref(nplan), P2, P16, 160, NULL) == mxq.MXQ_EALIGN
+    assert ngo(ctypes.byref(nplan), P16, NULL, 160, NULL) == mxq.MXQ_EINVAL
+    assert ngo(ctypes.byref(nplan), P16, P8, 160, NULL) == mxq.MXQ_EALIGN
+    assert ngo(ctypes.byref(nplan), P16, P16, 159, NULL) == mxq.MXQ_ESIZE
+    for field, value in [("kind", 0), ("n_entries", 1), ("workspace_bytes", 128),
+                         ("n_groups", 0)]:
+        alt = mxq.GroupedPlan.from_buffer_copy(nplan)
+        setattr(alt, field, value)
+        assert ngo(ctypes.byref(alt), P16, P16, 160, NULL) == mxq.MXQ_EINVAL, field
+    assert go(ctypes.byref(nplan), P16, 160, NULL) == mxq.MXQ_EINVAL
