@@ -11,7 +11,10 @@ resident in HBM.  Prints one JSON line.
 Steps cycle through BATCHES resident batches, each with its own outputs
 (distinct HBM addresses, 2.8 GB in all), so no step finds its input in the
 256 MB Infinity Cache that the previous step just streamed through: the
-timed rate is an HBM rate.  Every other workload is timed the same way.
+timed rate is an HBM rate.  Every other workload is timed the same way, over
+enough copies of its inputs that at least 1 GB of other inputs is read between
+two reads of the same one (a kernel whose input is small, such as a
+dequantization, gets more copies).
 
 Besides the timed steps it reports, in the same line:
   roofline      the one-pass kernel's achieved GB/s (HIP events on the stream
@@ -39,7 +42,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 BATCHES = 4            # resident batches the main step loop cycles through
-ROTATE_BYTES = 1e9     # other workloads: enough copies to touch this much between reuses
+COLD_INPUT_BYTES = 1e9  # other workloads: input bytes read between two reads of one copy
+MAX_COPIES = 32
 METRIC = "MXFP8 quantize GB/s (bf16 in + fp8/scale out) and % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_mxfp8_amd", "csrc", f)
@@ -284,8 +288,10 @@ def main():
                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(nbytes),
                     "copies": len(launches)}
 
-        def ncopies(nbytes):
-            return int(min(8, max(2, -(-ROTATE_BYTES // nbytes))))
+        def ncopies(in_bytes):
+            """Copies of a workload whose launch reads in_bytes, so that
+            COLD_INPUT_BYTES of other copies pass between two reads of one."""
+            return int(min(MAX_COPIES, max(2, -(-COLD_INPUT_BYTES // in_bytes) + 1)))
 
         # the main tensor, one output family at a time (same batches)
         rb = 2 * e + e + e // 32
@@ -300,12 +306,22 @@ def main():
         breakdown["act_16384 fake-quant only"] = rotated(
             [lambda d=d: check(lib.mxq_fake_quant(P(d["x"]), rows, cols, 1, P(d["fq"]), sp),
                                "fake_quant") for d in batches], 4 * e)
+        def code_copies(qk, sk):
+            """Copies of the batches' codes and scales for a dequantization
+            (its input is half or less of a batch's), each with its own output."""
+            in_bytes = batches[0][qk].numel() + batches[0][sk].numel()
+            return [{"q": batches[i % BATCHES][qk].clone(), "s": batches[i % BATCHES][sk].clone(),
+                     "out": torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)}
+                    for i in range(ncopies(in_bytes))]
+
         # MXFP8 dequantization of the batches' codes, both axes
         for ax, qk, sk, nm in ((1, "qr", "sr", "row-wise"), (0, "qc", "sc", "column-wise")):
+            dq = code_copies(qk, sk)
             breakdown[f"act_16384 {nm} dequantize"] = rotated(
-                [lambda d=d, ax=ax, qk=qk, sk=sk: check(
-                    lib.mxq_dequantize(P(d[qk]), P(d[sk]), rows, cols, ax, P(d["fq"]), sp),
-                    "dequantize") for d in batches], e + batches[0][sk].numel() + 2 * e)
+                [lambda d=d, ax=ax: check(
+                    lib.mxq_dequantize(P(d["q"]), P(d["s"]), rows, cols, ax, P(d["out"]), sp),
+                    "dequantize") for d in dq], e + batches[0][sk].numel() + 2 * e)
+            del dq
         # column-wise in the transposed (backward-pass) layout, with and
         # without the row-wise outputs of the same pass
         breakdown["act_16384 one-pass, column-wise transposed"] = rotated(
@@ -335,11 +351,12 @@ def main():
         breakdown["act_16384 MXFP4 simulate-QAT (fake-quant only)"] = rotated(
             [lambda d=d: check(lib.mxfp4_fake_quant(P(d["x"]), rows, cols, P(d["fq"]), sp),
                                "mxfp4 fq") for d in batches], 4 * e)
+        dq = code_copies("q4", "s4")
         breakdown["act_16384 MXFP4 dequantize"] = rotated(
-            [lambda d=d: check(lib.mxfp4_dequantize(P(d["q4"]), P(d["s4"]), rows, cols, P(d["fq"]),
-                                                    sp), "mxfp4 dq") for d in batches],
+            [lambda d=d: check(lib.mxfp4_dequantize(P(d["q"]), P(d["s"]), rows, cols, P(d["out"]),
+                                                    sp), "mxfp4 dq") for d in dq],
             e // 2 + e // 32 + 2 * e)
-        del batches
+        del batches, dq
         torch.cuda.empty_cache()
 
         # weight [4097, 7168] row-wise (pad-then-crop case)
@@ -349,7 +366,7 @@ def main():
         wbytes = 3 * wr * wc + wr * wc // 32
         wsets = [(w0.clone(), torch.empty((wr, wc), dtype=torch.uint8, device=dev),
                   torch.empty((wr, wc // 32), dtype=torch.uint8, device=dev))
-                 for _ in range(ncopies(wbytes))]
+                 for _ in range(ncopies(wr * wc * 2))]
         breakdown["weight_4097 row-wise"] = rotated(
             [lambda t=t: check(lib.mxq_quantize_rowwise(P(t[0]), wr, wc, wc, P(t[1]), wc, P(t[2]),
                                                         wc // 32, None, 0, sp), "rowwise")
@@ -425,8 +442,8 @@ def main():
         nwsz = lib.nvfp4_workspace_size()
         bbytes = 3 * ye + 4 * (n_ // 128) ** 2
         nbytes = 2 * ye + ye // 2 + ye // 16 + 4
-        ysets = []
-        for _ in range(ncopies(bbytes)):
+        ysets = []  # as many as the smallest input (NVFP4 dequantization's) needs
+        for _ in range(ncopies(ye // 2 + ye // 16)):
             ysets.append({
                 "y": y0.clone(),
                 "bq": torch.empty((n_, n_), dtype=torch.uint8, device=dev),

@@ -540,8 +540,8 @@ __global__ __launch_bounds__(256) void nvfp4_g_amax_kernel(const NvEntry *__rest
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     uint4 v[kRowsNv / 4];
-    nvfp4_load_rows<kNTLoadNvGAmax>(E.x, rb * kRowsNv + wave, E.rows, E.cols, seg * kSegNv + lane * 8,
-                                   v);
+    nvfp4_load_rows<kNTLoadNvGAmax>(global_ptr(E.x), rb * kRowsNv + wave, E.rows, E.cols,
+                                    seg * kSegNv + lane * 8, v);
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < kRowsNv / 4; ++i) m = max(m, amax8(v[i]));
@@ -597,10 +597,11 @@ __global__ __launch_bounds__(256) void nvfp4_g_quant_kernel(const NvEntry *__res
     const int64_t col = seg * kSegNv + lane * 8, r0 = rb * kRowsNv + wave;
     __shared__ float2 tab[128];
     uint4 v[kRowsNv / 4];
-    nvfp4_load_rows<kNTLoadNvQuant>(E.x, r0, E.rows, E.cols, col, v);
+    nvfp4_load_rows<kNTLoadNvQuant>(global_ptr(E.x), r0, E.rows, E.cols, col, v);
     const float g = gs[E.group];
     nvfp4_scale_table(tab, g);
-    nvfp4_encode_rows(v, r0, E.rows, E.cols, col, E.q, E.s, g, g != g, tab);
+    nvfp4_encode_rows(v, r0, E.rows, E.cols, col, global_ptr(E.q), global_ptr(E.s), g, g != g,
+                      tab);
 }
 
 // 8 packed E2M1 nibbles (one word) -> 8 bf16, effective scale eff.
@@ -649,20 +650,27 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__res
     const int64_t col = seg * kSegNv + lane * 8;
     if (col >= cols) return;  // cols % 16 == 0; no barriers below
     const int64_t r0 = rb * kRowsNv + wave;
-    const float g = *g_in;
     constexpr int kR = kRowsNv / 4;
-    uint32_t pk[kR];
-    float eff[kR];
-    bool bad = false;
+    uint32_t pk[kR], sb[kR];
+    // all 8 rows' loads are issued before any is used (decoding a scale in
+    // this loop made the compiler wait for each row's loads in turn)
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
         pk[i] = 0u;
-        eff[i] = 0.0f;
+        sb[i] = 0u;
         if (r < rows) {
             pk[i] = ld4<kNTLoadDq>(q + r * (cols >> 1) + (col >> 1));
-            eff[i] = e4m3_to_f32(s_in[r * (cols >> 4) + (col >> 4)]) * g;  // one IEEE fp32 multiplication
+            sb[i] = s_in[r * (cols >> 4) + (col >> 4)];
         }
+    }
+    const float g = *g_in;
+    float eff[kR];
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+        // one IEEE fp32 multiplication; rows past the end stay 0
+        eff[i] = r0 + 4 * i < rows ? e4m3_to_f32(sb[i]) * g : 0.0f;
         bad |= !__builtin_isfinite(eff[i]);  // NaN products (x * NaN, 0 * Inf) take the sign rule
     }
     const bool slow = wave_any(bad);

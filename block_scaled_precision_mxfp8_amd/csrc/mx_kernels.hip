@@ -556,8 +556,9 @@ __global__ __launch_bounds__(256) void mx_grouped_kernel(const GroupEntry *__res
     const GroupEntry E = table[lo];
     const int32_t local = t - starts[lo];
     const int32_t nseg = (int32_t)E.nseg;
-    mx_row_tile<true, false, kUGrouped>(E.x, E.rows, E.cols, E.ldx, E.q, E.ldq, E.scale, E.lds, nullptr, 0,
-                             local % nseg, local / nseg);
+    mx_row_tile<true, false, kUGrouped>(global_ptr(E.x), E.rows, E.cols, E.ldx, global_ptr(E.q),
+                                        E.ldq, global_ptr(E.scale), E.lds, nullptr, 0, local % nseg,
+                                        local / nseg);
 }
 
 // ---------------------------------------------------------------------------

@@ -87,6 +87,17 @@ __device__ __forceinline__ bool xcd_row_tile(int64_t nseg, int64_t nrb, int64_t 
     return rb < nrb;
 }
 
+// A pointer read from memory (an entry of a grouped launch table) carries no
+// address space, so the compiler would reach it with flat instructions, whose
+// completion waits also cover LDS and scalar loads.  Table pointers always
+// point to global memory; saying so gives global loads and stores.
+template <class T>
+__device__ __forceinline__ T *global_ptr(T *p)
+{
+    using G = __attribute__((address_space(1))) T *;
+    return (T *)(G)__builtin_bit_cast(uintptr_t, p);
+}
+
 // Index of the last entry whose first tile is <= t, for strictly increasing
 // starts[0..n) with starts[0] == 0 (grouped launches).  64-way search: each
 // round, lane k samples starts[lo + k*step]; the sampled values increase with
