@@ -24,7 +24,16 @@ namespace mxq {
 
 constexpr int kBlk = 128;   // block-FP8 tile edge
 constexpr int kSegNv = 512; // NVFP4 columns per wave segment (64 lanes x 8)
-constexpr int kRowsNv = 32; // NVFP4 rows per workgroup tile
+constexpr int kRowsNv = 32; // rows per workgroup tile of the grouped NVFP4 passes
+// Rows per tile of the single-tensor NVFP4 encoding pass: 16 measured 9%
+// faster than 32 there with cold inputs, while the grouped passes ran 3%
+// slower with 16.
+constexpr int kRowsNvQ = 16;
+// Rows per workgroup tile of the dequantizers, the 1 x 128 quantizer and the
+// FP8 -> MXFP8 pass (4 waves x 4 rows).  With cold inputs, 16-row tiles
+// measured 4-7% faster than 32-row ones, 8-row ones no faster.
+constexpr int kRowsDq = 16;
+static_assert(kBlk % kRowsDq == 0, "a tile's rows share one 128-row block row");
 // Streaming (non-temporal) hints, chosen by measurement on MI355X with
 // inputs read cold from HBM.  Outputs are written once.  Hinted 16-byte loads
 // of x help block-FP8 (+3%); the dequantizers' 4- and 8-byte code loads do
@@ -165,9 +174,10 @@ __device__ __forceinline__ uint4 bfp8_dequant8(uint2 c, float S, bool slow)
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Tiles: 512-column segment x 32 rows (4 waves x 8 rows).  128 x 128 blocks
-// (kRowScales false): a 32-row block lies inside one 128-row tile row, so each
-// lane needs one scale; 1 x 128 blocks (kRowScales true): one scale per row.
+// Tiles: 512-column segment x kRowsDq rows (4 waves x 4 rows).  128 x 128
+// blocks (kRowScales false): a tile's rows lie inside one 128-row block row,
+// so each lane needs one scale; 1 x 128 blocks (kRowScales true): one scale
+// per row.
 template <bool kRowScales>
 __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__restrict__ q,
                                                            const float *__restrict__ scale,
@@ -189,8 +199,8 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     if (col >= cols) return;  // cols % 8 == 0; no barriers below
-    const int64_t r0 = rb * kRowsNv + wave;
-    constexpr int kR = kRowsNv / 4;
+    const int64_t r0 = rb * kRowsDq + wave;
+    constexpr int kR = kRowsDq / 4;
     float S[kR];
     uint2 c[kR];
     bool bad = false;
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
         if (kRowScales) {
             if (r < rows) S[i] = scale[r * tc + col / kBlk];
         } else {
-            S[i] = i == 0 ? scale[((rb * kRowsNv) / kBlk) * tc + col / kBlk] : S[0];
+            S[i] = i == 0 ? scale[((rb * kRowsDq) / kBlk) * tc + col / kBlk] : S[0];
         }
         if (r < rows) c[i] = ld8<kNTLoadDq>(q + r * cols + col);
         const uint32_t tx = c[i].x & 0x7F7F7F7Fu, ty = c[i].y & 0x7F7F7F7Fu;
@@ -246,8 +256,8 @@ __global__ __launch_bounds__(256) void bfp8_1x128_kernel(const uint16_t *__restr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     const bool cin = col < cols;  // cols % 8 == 0; lanes past the edge still join the DPP
-    const int64_t r0 = rb * kRowsNv + wave;
-    constexpr int kR = kRowsNv / 4;
+    const int64_t r0 = rb * kRowsDq + wave;
+    constexpr int kR = kRowsDq / 4;
     uint4 v[kR];
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
@@ -302,9 +312,9 @@ __global__ __launch_bounds__(256) void bfp8_to_mx_kernel(const uint8_t *__restri
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     if (col >= cols) return;  // cols % 32 == 0: whole quads leave; no barriers below
-    const int64_t r0 = rb * kRowsNv + wave;
-    const float S = scale[((rb * kRowsNv) / kBlk) * tc + col / kBlk];
-    constexpr int kR = kRowsNv / 4;
+    const int64_t r0 = rb * kRowsDq + wave;
+    const float S = scale[((rb * kRowsDq) / kBlk) * tc + col / kBlk];
+    constexpr int kR = kRowsDq / 4;
     uint2 c[kR];
     bool nan_code = false;
 #pragma unroll
@@ -402,9 +412,10 @@ __device__ __forceinline__ uint32_t nvfp4_codes8(const uint4 a, float eff, float
     return out;
 }
 
-// Tiles: 512-column segment x 32 rows (4 waves x 8 rows).  Lane pair
-// (2k, 2k+1) holds one 16-element block, 8 elements each, so every load and
-// store instruction of a wave is contiguous; the block amax is one DPP swap.
+// Tiles: 512-column segment x kRowsNvQ rows (single tensor) or kRowsNv rows
+// (grouped); wave w of a tile holds rows w, w + 4, ...  Lane pair (2k, 2k+1)
+// holds one 16-element block, 8 elements each, so every load and store
+// instruction of a wave is contiguous; the block amax is one DPP swap.
 //
 // With g fixed for the workgroup, a block's effective scale can take only 127
 // values, one per E4M3 magnitude code: the workgroup tabulates
@@ -420,12 +431,13 @@ __device__ __forceinline__ void nvfp4_scale_table(float2 *tab, float g)
     __syncthreads();
 }
 
-// The per-block steps for one wave's 8 rows of a tile (rows r0 + 4i), given
+// The per-block steps for one wave's kR rows of a tile (rows r0 + 4i), given
 // the global scale g (NaN when the tensor or scale group holds NaN/Inf) and
 // the workgroup's table for g.  The block-scale quotient b / (6g) is IEEE
 // division's result either way: by the reciprocal-FMA step when 6g lies in
 // its proven domain (b <= A keeps the quotient under 449), else by division.
-__device__ __forceinline__ void nvfp4_encode_rows(const uint4 (&v)[kRowsNv / 4], int64_t r0,
+template <int kR>
+__device__ __forceinline__ void nvfp4_encode_rows(const uint4 (&v)[kR], int64_t r0,
                                                   int64_t rows, int64_t cols, int64_t col,
                                                   uint8_t *__restrict__ q,
                                                   uint8_t *__restrict__ s_out, float g,
@@ -436,7 +448,7 @@ __device__ __forceinline__ void nvfp4_encode_rows(const uint4 (&v)[kRowsNv / 4],
     const bool dfast = markstein_ok(d);           // uniform: g is the workgroup's
     const float yd = dfast ? 1.0f / d : 0.0f;     // RN(1 / d), one IEEE division per thread
 #pragma unroll
-    for (int i = 0; i < kRowsNv / 4; ++i) {
+    for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
         const bool ok = cin && r < rows;
         const uint32_t h = amax8(v[i]);
@@ -466,14 +478,14 @@ __device__ __forceinline__ void nvfp4_encode_rows(const uint4 (&v)[kRowsNv / 4],
     }
 }
 
-// This wave's 8 rows of a tile (16 bytes of x per lane and row).
-template <bool kNT>
+// This wave's kR rows of a tile (16 bytes of x per lane and row).
+template <bool kNT, int kR>
 __device__ __forceinline__ void nvfp4_load_rows(const uint16_t *__restrict__ x, int64_t r0,
                                                 int64_t rows, int64_t cols, int64_t col,
-                                                uint4 (&v)[kRowsNv / 4])
+                                                uint4 (&v)[kR])
 {
 #pragma unroll
-    for (int i = 0; i < kRowsNv / 4; ++i) {
+    for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
         v[i] = make_uint4(0, 0, 0, 0);
         if (col < cols && r < rows) v[i] = ld16<kNT>(x + r * cols + col);
@@ -511,9 +523,9 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
-    const int64_t r0 = rb * kRowsNv + wave;
+    const int64_t r0 = rb * kRowsNvQ + wave;
     __shared__ float2 tab[128];
-    uint4 v[kRowsNv / 4];
+    uint4 v[kRowsNvQ / 4];
     nvfp4_load_rows<kNTLoadNvQuant>(x, r0, rows, cols, col, v);
     const float g = *g_in;
     nvfp4_scale_table(tab, g);
@@ -644,16 +656,16 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(const uint8_t *__res
                                                             int64_t nseg)
 {
     int64_t seg, rb;
-    if (!xcd_row_tile(nseg, (rows + kRowsNv - 1) / kRowsNv, seg, rb)) return;
+    if (!xcd_row_tile(nseg, (rows + kRowsDq - 1) / kRowsDq, seg, rb)) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     if (col >= cols) return;  // cols % 16 == 0; no barriers below
-    const int64_t r0 = rb * kRowsNv + wave;
-    constexpr int kR = kRowsNv / 4;
+    const int64_t r0 = rb * kRowsDq + wave;
+    constexpr int kR = kRowsDq / 4;
     uint32_t pk[kR], sb[kR];
-    // all 8 rows' loads are issued before any is used (decoding a scale in
-    // this loop made the compiler wait for each row's loads in turn)
+    // all of the wave's loads are issued before any is used (decoding a
+    // scale in this loop made the compiler wait for each row's loads in turn)
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
@@ -703,7 +715,7 @@ hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t sli
                                hipStream_t stream)
 {
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t per = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    const int64_t per = nseg * ((rows + kRowsDq - 1) / kRowsDq);
     if (per <= 0 || slices <= 0) return hipSuccess;
     if (per > 0x7FFFFFFF / slices) return hipErrorInvalidConfiguration;
     const int64_t tiles = per * slices;
@@ -723,7 +735,7 @@ hipError_t launch_bfp8_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint
 {
     const int64_t tc = (cols + kBlk - 1) / kBlk;
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    const int64_t tiles = nseg * ((rows + kRowsDq - 1) / kRowsDq);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);
@@ -744,7 +756,7 @@ hipError_t launch_bfp8_to_mx(const uint8_t *q, const float *scale, int64_t rows,
 {
     const int64_t tc = (cols + kBlk - 1) / kBlk;
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    const int64_t tiles = nseg * ((rows + kRowsDq - 1) / kRowsDq);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bfp8_to_mx_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scale,
@@ -760,7 +772,7 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     const int64_t want = (nvec + 255) / 256;
     const int ablocks = (int)(want < kNvAmaxBlocks ? want : kNvAmaxBlocks);
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsNv - 1) / kRowsNv);
+    const int64_t tiles = nseg * ((rows + kRowsNvQ - 1) / kRowsNvQ);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
     hipError_t err = hipGetLastError();
@@ -805,7 +817,7 @@ hipError_t launch_nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float 
                                 int64_t cols, uint16_t *out, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t nrb = (rows + kRowsNv - 1) / kRowsNv;
+    const int64_t nrb = (rows + kRowsDq - 1) / kRowsDq;
     if (nseg <= 0 || nrb <= 0) return hipSuccess;
     const int64_t tiles = xcd_row_grid(nseg, nrb);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;

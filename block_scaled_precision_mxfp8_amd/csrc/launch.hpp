@@ -9,7 +9,7 @@ namespace mxq {
 
 // Launch table entry for the grouped row-wise kernel (staged in the caller's
 // device workspace, followed by an int32 array of each entry's first tile).
-// Tiles are (512-column segment, 32-row block) pairs, numbered tensor by
+// Tiles are (512-column segment, 16-row block) pairs, numbered tensor by
 // tensor; one workgroup runs one tile.
 struct GroupEntry {
     const uint16_t *x;

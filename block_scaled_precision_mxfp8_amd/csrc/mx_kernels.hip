@@ -24,11 +24,15 @@
 namespace mxq {
 
 constexpr int kSeg = 512;          // columns per wave segment
-constexpr int kRowsPerTile = 32;   // rows per row-wise workgroup tile (4 waves x 8 rows)
-// Rows each wave keeps in flight per step.  Single tensors: all 8 of its tile
-// rows (+3% row-wise and fake-quant on MI355X over 4); the grouped launch
-// does 1% better with 4.
-constexpr int kURow = 8;
+// Rows per row-wise workgroup tile (4 waves x 4 rows).  With cold inputs on
+// [16384, 7168], 16-row tiles measured faster than 32-row ones: row-wise 1-2%,
+// fake-quant 4%, the grouped MoE launch 6%.
+constexpr int kRowsPerTile = 16;
+// Rows per dequantize tile (4 waves x 4 rows): 3% (row groups) and 7%
+// (column groups) faster than 32.
+constexpr int kRowsDq = 16;
+// Rows each wave keeps in flight per step: all 4 of its tile rows.
+constexpr int kURow = 4;
 constexpr int kUGrouped = 4;
 constexpr int kColTileRows = 128;  // rows per column-wise workgroup tile (4 waves x 32)
 // Streaming (non-temporal) hints on every load and store: each byte is
@@ -40,7 +44,7 @@ constexpr bool kNTLoad = true;
 constexpr bool kNTStore = true;
 
 // ---------------------------------------------------------------------------
-// Row-wise tile: rows [rb*32, rb*32+32) x columns of segment `seg`.
+// Row-wise tile: rows [rb*kRowsPerTile, (rb+1)*kRowsPerTile) x columns of segment `seg`.
 // kFull: the whole tile is inside the tensor (wave-uniform), so no load or
 // store needs a predicate.
 // ---------------------------------------------------------------------------
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 
 // ---------------------------------------------------------------------------
 // Dequantize: out = bf16_RNE(E4M3(q) * 2^(s - 127)), row (axis 1) or column
-// (axis 0) groups.  Tiles as the row-wise kernel.
+// (axis 0) groups.  Tiles: 512-column segment x kRowsDq rows.
 // ---------------------------------------------------------------------------
 template <int kAxis>
 __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restrict__ q,
@@ -457,15 +461,16 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSeg + lane * 8;
     if (col >= cols) return;  // no barriers below
-    const int64_t r0 = rb * kRowsPerTile + wave;
-    // all 8 rows' codes and scales in flight before any is decoded
-    constexpr int kR = kRowsPerTile / 4;
+    const int64_t r0 = rb * kRowsDq + wave;
+    // all of the wave's codes and scales in flight before any is decoded
+    constexpr int kR = kRowsDq / 4;
     uint2 cc[kR];
     uint32_t ss[kR];
-    // column groups: the tile's 32 rows are one group row, so one scale load
-    static_assert(kRowsPerTile == 32, "a dequantize tile spans exactly one column-group row");
+    // column groups: the tile's rows lie in one group row, so one scale load
+    static_assert(32 % kRowsDq == 0, "a dequantize tile lies in one column-group row");
+    const int64_t grow = (rb * kRowsDq) >> 5;  // the tile's column-group row
     const uint2 sv = kAxis == 0 && r0 < rows
-                         ? *reinterpret_cast<const uint2 *>(scale + rb * cols + col)
+                         ? *reinterpret_cast<const uint2 *>(scale + grow * cols + col)
                          : make_uint2(0, 0);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
@@ -661,8 +666,8 @@ hipError_t launch_e8m0_to_f32(const uint8_t *scale, int64_t n, float *out, hipSt
 hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
                              int axis, uint16_t *out, hipStream_t stream)
 {
-    int64_t nseg = 0;
-    const int64_t tiles = mx_row_tiles(rows, cols, &nseg);
+    const int64_t nseg = (cols + kSeg - 1) / kSeg;
+    const int64_t tiles = nseg * ((rows + kRowsDq - 1) / kRowsDq);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);

@@ -369,9 +369,10 @@ def test_e8m0_to_fp32_errors(lib):
 
 def test_grouped_plan_build_and_refusals(lib):
     """Building a grouped plan runs on the host only: the table image holds
-    every non-empty descriptor with its first tile (tiles are 512-column x
-    32-row blocks, numbered tensor by tensor), and a launch refuses a missing,
-    foreign or altered plan before anything reaches the GPU."""
+    every non-empty descriptor with its first tile (tiles are 512-column
+    blocks of 16 rows for MXFP8 and 32 rows for NVFP4, numbered tensor by
+    tensor), and a launch refuses a missing, foreign or altered plan before
+    anything reaches the GPU."""
     import numpy as np
     b = lib.mxq_grouped_plan_build
     descs = (mxq.GroupDesc * 3)()
@@ -383,15 +384,15 @@ def test_grouped_plan_build_and_refusals(lib):
     assert b(descs, -1, ctypes.byref(plan), NULL, 0) == mxq.MXQ_EINVAL
     assert b(NULL, 3, ctypes.byref(plan), NULL, 0) == mxq.MXQ_EINVAL
     assert b(descs, 3, ctypes.byref(plan), NULL, 0) == mxq.MXQ_OK      # sizes only
-    assert (plan.n_entries, plan.n_groups, plan.total_tiles) == (2, 0, 3 * 2 + 1)
+    assert (plan.n_entries, plan.n_groups, plan.total_tiles) == (2, 0, 3 * 3 + 1)
     assert plan.table_bytes == 176 and plan.workspace_bytes == 176    # 2 x (80 + 4), to 16
     img = (ctypes.c_ubyte * 176)()
     assert b(descs, 3, ctypes.byref(plan), img, 175) == mxq.MXQ_ESIZE
     assert b(descs, 3, ctypes.byref(plan), img, 176) == mxq.MXQ_OK
     w = np.frombuffer(bytes(img), dtype=np.int64, count=20)
     assert list(w[:10]) == [0x10000, 0x20000, 0x30000, 40, 1056, 1056, 1056, 33, 0, 3]
-    assert list(w[10:]) == [0x40000, 0x50000, 0x60000, 8, 64, 72, 64, 2, 6, 1]
-    assert list(np.frombuffer(bytes(img), dtype=np.int32, offset=160, count=2)) == [0, 6]
+    assert list(w[10:]) == [0x40000, 0x50000, 0x60000, 8, 64, 72, 64, 2, 9, 1]
+    assert list(np.frombuffer(bytes(img), dtype=np.int32, offset=160, count=2)) == [0, 9]
     bad_desc = (mxq.GroupDesc * 1)(mxq.GroupDesc(0x10000, 0x20000, 0x30000, 8, 48, 48, 48, 2))
     assert b(bad_desc, 1, ctypes.byref(plan), NULL, 0) == mxq.MXQ_ESHAPE
     assert plan.n_entries == 2                                         # untouched on error
