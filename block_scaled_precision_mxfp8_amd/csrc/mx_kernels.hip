@@ -136,21 +136,20 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
 // column).  (The x-layout column-wise kernel, mx_colwise_kernel, splits each
 // group over several waves instead.)
 // ---------------------------------------------------------------------------
-// kColT: column codes go to the transposed layout instead: staged in LDS as
+// Column codes go to the transposed layout: staged in LDS as
 // lds_t[column slot][row] (column slot j*64 + lane for the lane's column j,
 // kTPitch dwords per slot) for the workgroup to write out as whole rows of
 // qt; the column scales are staged after them, one dword (the workgroup's 4
 // groups) per column, for st [cols, nrg].
 constexpr int kTPitch = 33;  // dwords per LDS column slot: 128 rows of codes + 1 (no bank conflicts)
 
-template <bool kCol, bool kColT, bool kRow, bool kFQRow, bool kFQCol, bool kFull>
-__device__ __forceinline__ void mx_colwise_body(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qc,
-    uint8_t *__restrict__ sc, uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
-    uint16_t *__restrict__ fq_row, uint16_t *__restrict__ fq_col, int64_t g, int64_t col,
-    uint32_t *__restrict__ lds_t, uint8_t *__restrict__ st, int64_t nrg)
+template <bool kRow, bool kFQRow, bool kFull>
+__device__ __forceinline__ void mx_colwise_t_body(const uint16_t *__restrict__ x, int64_t rows,
+                                                  int64_t cols, uint8_t *__restrict__ qr,
+                                                  uint8_t *__restrict__ sr,
+                                                  uint16_t *__restrict__ fq_row, int64_t g,
+                                                  int64_t col, uint32_t *__restrict__ lds_t)
 {
-    constexpr bool kColAny = kCol || kColT || kFQCol;
     constexpr bool kRowAny = kRow || kFQRow;
     const bool cin = kFull || col < cols;
     const int64_t r0 = g * 32;
@@ -165,13 +164,13 @@ __device__ __forceinline__ void mx_colwise_body(
     }
 
     // column scales: in-lane amax over the 32 rows, one E8M0 byte per column
-    uint32_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    bool nan[8] = {false, false, false, false, false, false, false, false};
-    bool col_slow = false;
-    uint32_t lim2[4] = {0, 0, 0, 0};
-    float sf[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int e[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (kColAny) {
+    uint32_t s[8];
+    bool nan[8];
+    uint32_t lim2[4];
+    float sf[8];
+    int e[8];
+    bool col_slow;
+    {
         uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
@@ -194,12 +193,7 @@ __device__ __forceinline__ void mx_colwise_body(
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             lim2[k] = mx_limit_bf16(s[2 * k]) | (mx_limit_bf16(s[2 * k + 1]) << 16);
-        if (kCol && cin) {
-            const uint32_t lo = s[0] | (s[1] << 8) | (s[2] << 16) | (s[3] << 24);
-            const uint32_t hi = s[4] | (s[5] << 8) | (s[6] << 16) | (s[7] << 24);
-            st8<kNTStore>(sc + g * cols + col, make_uint2(lo, hi));
-        }
-        if (kColT && cin) {
+        if (cin) {
             // byte `wave` of the column's dword: the workgroup's 4 groups of it
             uint8_t *lds_s = reinterpret_cast<uint8_t *>(lds_t + kSeg * kTPitch);
             const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -209,25 +203,6 @@ __device__ __forceinline__ void mx_colwise_body(
         }
         col_slow = wave_any(any_nan);  // a NaN/Inf column in the wave: exact software path
     }
-
-    // one row of column codes (and its column-wise fake-quant) out
-    auto put_col_row = [&](int i, uint32_t c0, uint32_t c1) __attribute__((always_inline)) {
-        const int64_t r = r0 + i;
-        const bool ok = kFull || (cin && r < rows);
-        if (kCol && ok) st8<kNTStore>(qc + r * cols + col, make_uint2(c0, c1));
-        if (kFQCol) {
-            uint32_t bb[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bb[j] = mx_dequant1((c0 >> (8 * j)) & 0xFFu, (int)s[j] - 7, nan[j]);
-                bb[4 + j] = mx_dequant1((c1 >> (8 * j)) & 0xFFu, (int)s[4 + j] - 7, nan[4 + j]);
-            }
-            if (ok)
-                st16<kNTStore>(fq_col + r * cols + col,
-                               make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16),
-                                          bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16)));
-        }
-    };
 
     // one row's row-wise codes and scale byte (do_q) and fake-quant (do_fq) out
     auto row_work = [&](int i, bool do_q, bool do_fq) __attribute__((always_inline)) {
@@ -253,7 +228,7 @@ __device__ __forceinline__ void mx_colwise_body(
         }
     };
 
-    // kColT: codes of rows i-2, i-1 wait here until rows i, i+1 complete a 4-row
+    // codes of rows i-2, i-1 wait here until rows i, i+1 complete a 4-row
     // dword per column
     uint32_t tq[4] = {0u, 0u, 0u, 0u};
     const int lane = threadIdx.x & (kWave - 1);
@@ -261,7 +236,7 @@ __device__ __forceinline__ void mx_colwise_body(
 
     static_for<0, 32, 2>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
-        if (kColAny) {
+        {
             uint32_t a0, a1, b0, b1;  // rows i and i+1: columns 0-3 and 4-7 of the lane
             if (!col_slow) {
                 // the pair fed to one convert shares a scale: same column, rows i and i+1
@@ -286,9 +261,7 @@ __device__ __forceinline__ void mx_colwise_body(
                 b1 = e4m3x4_col(v[i + 1].z, v[i + 1].w, e[4], e[5], e[6], e[7], nan[4], nan[5],
                                 nan[6], nan[7]);
             }
-            put_col_row(i, a0, a1);
-            put_col_row(i + 1, b0, b1);
-            if (kColT) {
+            {
                 if (i % 4 == 0) {
                     tq[0] = a0; tq[1] = a1; tq[2] = b0; tq[3] = b1;
                 } else {
@@ -545,11 +518,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int64_t nrg = (rows + 31) / 32;
     if (g * 32 < rows) {  // wave-uniform; every wave reaches the barrier below
         if ((seg + 1) * kSeg <= cols && g * 32 + 32 <= rows)
-            mx_colwise_body<false, true, kRow, kFQRow, false, true>(
-                x, rows, cols, nullptr, nullptr, qr, sr, fq_row, nullptr, g, col, lds_t, st, nrg);
+            mx_colwise_t_body<kRow, kFQRow, true>(x, rows, cols, qr, sr, fq_row, g, col, lds_t);
         else
-            mx_colwise_body<false, true, kRow, kFQRow, false, false>(
-                x, rows, cols, nullptr, nullptr, qr, sr, fq_row, nullptr, g, col, lds_t, st, nrg);
+            mx_colwise_t_body<kRow, kFQRow, false>(x, rows, cols, qr, sr, fq_row, g, col, lds_t);
     }
     __syncthreads();
     {
