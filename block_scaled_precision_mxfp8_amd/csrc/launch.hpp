@@ -40,7 +40,8 @@ hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t row
 hipError_t launch_mx_grouped(const GroupEntry *table_dev, const int32_t *starts_dev, int32_t n,
                              int64_t total_tiles, hipStream_t stream);
 
-int64_t mx_row_tiles(int64_t rows, int64_t cols, int64_t *nseg);
+// Tiles of one tensor in a grouped row-wise launch (and its 512-column segments).
+int64_t mx_grouped_tiles(int64_t rows, int64_t cols, int64_t *nseg);
 
 hipError_t launch_mx4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
                             uint8_t *scale, uint16_t *fq, hipStream_t stream);

@@ -24,16 +24,16 @@
 namespace mxq {
 
 constexpr int kSeg = 512;          // columns per wave segment
-// Rows per row-wise workgroup tile (4 waves x 4 rows).  With cold inputs on
-// [16384, 7168], 16-row tiles measured faster than 32-row ones: row-wise 1-2%,
-// fake-quant 4%, the grouped MoE launch 6%.
-constexpr int kRowsPerTile = 16;
+// Rows per row-wise workgroup tile; each of the 4 waves keeps all its rows in
+// flight.  With cold inputs on [16384, 7168], against 32-row tiles: 16 rows
+// made row-wise 1-2%, fake-quant 4% and the grouped MoE launch 6% faster;
+// 8 rows gained another 2% (row-wise) and 1.6% (fake-quant) for single
+// tensors but lost 4.5% on the grouped launch.
+constexpr int kRowsRow = 8;       // single tensor (4 waves x 2 rows)
+constexpr int kRowsGrouped = 16;  // grouped launch (4 waves x 4 rows)
 // Rows per dequantize tile (4 waves x 4 rows): 3% (row groups) and 7%
 // (column groups) faster than 32.
 constexpr int kRowsDq = 16;
-// Rows each wave keeps in flight per step: all 4 of its tile rows.
-constexpr int kURow = 4;
-constexpr int kUGrouped = 4;
 constexpr int kColTileRows = 128;  // rows per transposed column-wise workgroup tile (4 waves x 32)
 // Streaming (non-temporal) hints on every load and store: each byte is
 // touched once.  Measured on MI355X with the [16384, 7168] activation read
@@ -44,11 +44,11 @@ constexpr bool kNTLoad = true;
 constexpr bool kNTStore = true;
 
 // ---------------------------------------------------------------------------
-// Row-wise tile: rows [rb*kRowsPerTile, (rb+1)*kRowsPerTile) x columns of segment `seg`.
+// Row-wise tile: rows [rb*kRowsT, (rb+1)*kRowsT) x columns of segment `seg`.
 // kFull: the whole tile is inside the tensor (wave-uniform), so no load or
 // store needs a predicate.
 // ---------------------------------------------------------------------------
-template <bool kQ, bool kFQ, bool kFull, int kU>
+template <bool kQ, bool kFQ, bool kFull, int kRowsT>
 __device__ __forceinline__ void mx_row_tile_impl(const uint16_t *__restrict__ x, int64_t rows,
                                                  int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
                                                  int64_t ldq, uint8_t *__restrict__ scale,
@@ -59,10 +59,11 @@ __device__ __forceinline__ void mx_row_tile_impl(const uint16_t *__restrict__ x,
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSeg + lane * 8;
     const bool cin = kFull || col < cols;  // cols % 32 == 0: a quad is all in or all out
-    const int64_t r0 = rb * kRowsPerTile + wave;
+    const int64_t r0 = rb * kRowsT + wave;
+    constexpr int kU = kRowsT / 4;  // the wave's rows, all in flight at once
 
 #pragma unroll
-    for (int it = 0; it < kRowsPerTile / (4 * kU); ++it) {
+    for (int it = 0; it < kRowsT / (4 * kU); ++it) {
         uint4 v[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
@@ -99,19 +100,19 @@ __device__ __forceinline__ void mx_row_tile_impl(const uint16_t *__restrict__ x,
     }
 }
 
-template <bool kQ, bool kFQ, int kU>
+template <bool kQ, bool kFQ, int kRowsT>
 __device__ __forceinline__ void mx_row_tile(const uint16_t *__restrict__ x, int64_t rows,
                                             int64_t cols, int64_t ldx, uint8_t *__restrict__ q,
                                             int64_t ldq, uint8_t *__restrict__ scale, int64_t lds,
                                             uint16_t *__restrict__ fq, int64_t ldf, int64_t seg,
                                             int64_t rb)
 {
-    if ((seg + 1) * kSeg <= cols && (rb + 1) * kRowsPerTile <= rows)
-        mx_row_tile_impl<kQ, kFQ, true, kU>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, seg,
-                                            rb);
+    if ((seg + 1) * kSeg <= cols && (rb + 1) * kRowsT <= rows)
+        mx_row_tile_impl<kQ, kFQ, true, kRowsT>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf,
+                                                seg, rb);
     else
-        mx_row_tile_impl<kQ, kFQ, false, kU>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, seg,
-                                             rb);
+        mx_row_tile_impl<kQ, kFQ, false, kRowsT>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf,
+                                                 seg, rb);
 }
 
 template <bool kQ, bool kFQ>
@@ -123,8 +124,8 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
                                                          int64_t nseg)
 {
     const int64_t tile = blockIdx.x;
-    mx_row_tile<kQ, kFQ, kURow>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, tile % nseg,
-                                tile / nseg);
+    mx_row_tile<kQ, kFQ, kRowsRow>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, tile % nseg,
+                                   tile / nseg);
 }
 
 // ---------------------------------------------------------------------------
@@ -681,7 +682,7 @@ __global__ __launch_bounds__(256) void mx_grouped_kernel(const GroupEntry *__res
     const GroupEntry E = table[lo];
     const int32_t local = t - starts[lo];
     const int32_t nseg = (int32_t)E.nseg;
-    mx_row_tile<true, false, kUGrouped>(global_ptr(E.x), E.rows, E.cols, E.ldx, global_ptr(E.q),
+    mx_row_tile<true, false, kRowsGrouped>(global_ptr(E.x), E.rows, E.cols, E.ldx, global_ptr(E.q),
                                         E.ldq, global_ptr(E.scale), E.lds, nullptr, 0, local % nseg,
                                         local / nseg);
 }
@@ -690,19 +691,19 @@ __global__ __launch_bounds__(256) void mx_grouped_kernel(const GroupEntry *__res
 // Host launchers
 // ---------------------------------------------------------------------------
 
-int64_t mx_row_tiles(int64_t rows, int64_t cols, int64_t *nseg)
+int64_t mx_grouped_tiles(int64_t rows, int64_t cols, int64_t *nseg)
 {
     const int64_t ns = (cols + kSeg - 1) / kSeg;
     if (nseg) *nseg = ns;
-    return ns * ((rows + kRowsPerTile - 1) / kRowsPerTile);
+    return ns * ((rows + kRowsGrouped - 1) / kRowsGrouped);
 }
 
 hipError_t launch_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t *q, int64_t ldq, uint8_t *scale, int64_t lds, uint16_t *fq,
                              int64_t ldf, hipStream_t stream)
 {
-    int64_t nseg = 0;
-    const int64_t tiles = mx_row_tiles(rows, cols, &nseg);
+    const int64_t nseg = (cols + kSeg - 1) / kSeg;
+    const int64_t tiles = nseg * ((rows + kRowsRow - 1) / kRowsRow);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);

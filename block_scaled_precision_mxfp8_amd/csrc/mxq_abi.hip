@@ -103,7 +103,7 @@ mxq_status mx_build(const mxq_group_desc *descs, int32_t n, std::vector<unsigned
         e.ldq = d.ldq;
         e.lds = d.lds;
         e.tile_begin = tiles;
-        const int64_t t = mxq::mx_row_tiles(d.rows, d.cols, &e.nseg);
+        const int64_t t = mxq::mx_grouped_tiles(d.rows, d.cols, &e.nseg);
         if (__builtin_add_overflow(tiles, t, &tiles) || tiles > 0x7FFFFFFF) return MXQ_ESIZE;
         table.push_back(e);
         starts.push_back((int32_t)e.tile_begin);
