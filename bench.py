@@ -272,9 +272,12 @@ def main():
     if not args.no_breakdown:
         def rotated(launches, nbytes, iters=20):
             """Back-to-back launches cycling through copies with their own
-            buffers; per-launch time = total / iters."""
-            for fn in launches:
-                fn()
+            buffers; per-launch time = total / iters.  The untimed warm-up
+            touches every copy and runs at least 16 launches, so that the
+            first workload after the CPU baseline is not timed while the GPU
+            is still leaving its idle clocks."""
+            for i in range(max(len(launches), 16)):
+                launches[i % len(launches)]()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
