@@ -29,11 +29,16 @@ constexpr int kRowsNv = 32; // rows per workgroup tile of the grouped NVFP4 pass
 // faster than 32 there with cold inputs, while the grouped passes ran 3%
 // slower with 16.
 constexpr int kRowsNvQ = 16;
-// Rows per workgroup tile of the dequantizers, the 1 x 128 quantizer and the
-// FP8 -> MXFP8 pass (4 waves x 4 rows).  With cold inputs, 16-row tiles
-// measured 4-7% faster than 32-row ones, 8-row ones no faster.
+// Rows per workgroup tile of the NVFP4 dequantizer and the FP8 -> MXFP8 pass
+// (4 waves x 4 rows).  With cold inputs, 16-row tiles measured 6-7% faster
+// than 32-row ones, 8-row ones no faster.
 constexpr int kRowsDq = 16;
-static_assert(kBlk % kRowsDq == 0, "a tile's rows share one 128-row block row");
+// Rows per tile of the block-FP8 dequantizer and the 1 x 128 quantizer (4
+// waves x 2 rows): 8 rows measured 5% (dequantize) and 4% (1 x 128
+// simulate-QAT) faster than 16, which were 4-7% faster than 32.
+constexpr int kRowsBq = 8;
+static_assert(kBlk % kRowsDq == 0 && kBlk % kRowsBq == 0,
+              "a tile's rows share one 128-row block row");
 // Streaming (non-temporal) hints, chosen by measurement on MI355X with
 // inputs read cold from HBM.  Outputs are written once.  Hinted 16-byte loads
 // of x help block-FP8 (+3%); the dequantizers' 4- and 8-byte code loads do
@@ -174,7 +179,7 @@ __device__ __forceinline__ uint4 bfp8_dequant8(uint2 c, float S, bool slow)
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Tiles: 512-column segment x kRowsDq rows (4 waves x 4 rows).  128 x 128
+// Tiles: 512-column segment x kRowsBq rows (4 waves x 2 rows).  128 x 128
 // blocks (kRowScales false): a tile's rows lie inside one 128-row block row,
 // so each lane needs one scale; 1 x 128 blocks (kRowScales true): one scale
 // per row.
@@ -199,8 +204,8 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     if (col >= cols) return;  // cols % 8 == 0; no barriers below
-    const int64_t r0 = rb * kRowsDq + wave;
-    constexpr int kR = kRowsDq / 4;
+    const int64_t r0 = rb * kRowsBq + wave;
+    constexpr int kR = kRowsBq / 4;
     float S[kR];
     uint2 c[kR];
     bool bad = false;
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(256) void bfp8_dequant_kernel(const uint8_t *__rest
         if (kRowScales) {
             if (r < rows) S[i] = scale[r * tc + col / kBlk];
         } else {
-            S[i] = i == 0 ? scale[((rb * kRowsDq) / kBlk) * tc + col / kBlk] : S[0];
+            S[i] = i == 0 ? scale[((rb * kRowsBq) / kBlk) * tc + col / kBlk] : S[0];
         }
         if (r < rows) c[i] = ld8<kNTLoadDq>(q + r * cols + col);
         const uint32_t tx = c[i].x & 0x7F7F7F7Fu, ty = c[i].y & 0x7F7F7F7Fu;
@@ -256,8 +261,8 @@ __global__ __launch_bounds__(256) void bfp8_1x128_kernel(const uint16_t *__restr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
     const bool cin = col < cols;  // cols % 8 == 0; lanes past the edge still join the DPP
-    const int64_t r0 = rb * kRowsDq + wave;
-    constexpr int kR = kRowsDq / 4;
+    const int64_t r0 = rb * kRowsBq + wave;
+    constexpr int kR = kRowsBq / 4;
     uint4 v[kR];
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
@@ -715,7 +720,7 @@ hipError_t launch_bfp8_dequant(const uint8_t *q, const float *scale, int64_t sli
                                hipStream_t stream)
 {
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t per = nseg * ((rows + kRowsDq - 1) / kRowsDq);
+    const int64_t per = nseg * ((rows + kRowsBq - 1) / kRowsBq);
     if (per <= 0 || slices <= 0) return hipSuccess;
     if (per > 0x7FFFFFFF / slices) return hipErrorInvalidConfiguration;
     const int64_t tiles = per * slices;
@@ -735,7 +740,7 @@ hipError_t launch_bfp8_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint
 {
     const int64_t tc = (cols + kBlk - 1) / kBlk;
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsDq - 1) / kRowsDq);
+    const int64_t tiles = nseg * ((rows + kRowsBq - 1) / kRowsBq);
     if (tiles <= 0) return hipSuccess;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);
