@@ -31,9 +31,10 @@ constexpr int kSeg = 512;          // columns per wave segment
 // tensors but lost 4.5% on the grouped launch.
 constexpr int kRowsRow = 8;       // single tensor (4 waves x 2 rows)
 constexpr int kRowsGrouped = 16;  // grouped launch (4 waves x 4 rows)
-// Rows per dequantize tile (4 waves x 4 rows): 3% (row groups) and 7%
-// (column groups) faster than 32.
-constexpr int kRowsDq = 16;
+// Rows per dequantize tile (4 waves x 2 rows).  Against 32-row tiles, 16 rows
+// were 3% (row groups) and 7% (column groups) faster, and 8 rows another 1%
+// and 1.5%.
+constexpr int kRowsDq = 8;
 constexpr int kColTileRows = 128;  // rows per transposed column-wise workgroup tile (4 waves x 32)
 // Streaming (non-temporal) hints on every load and store: each byte is
 // touched once.  Measured on MI355X with the [16384, 7168] activation read
@@ -582,9 +583,19 @@ __global__ __launch_bounds__(256) void mx_dequant_kernel(const uint8_t *__restri
                                                          int64_t rows, int64_t cols,
                                                          uint16_t *__restrict__ out, int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg;
-    const int64_t rb = tile / nseg;
+    int64_t seg, rb;
+    if (kAxis == 0) {
+        // the 32 / kRowsDq tiles of one column group run back to back on one
+        // XCD, so its scale row is fetched into one L2 once
+        constexpr int kSub = 32 / kRowsDq;
+        int64_t sp, gi;
+        if (!xcd_row_tile(nseg * kSub, (rows + 31) / 32, sp, gi)) return;
+        seg = sp / kSub;
+        rb = gi * kSub + sp % kSub;
+    } else {
+        seg = blockIdx.x % nseg;
+        rb = blockIdx.x / nseg;
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSeg + lane * 8;
@@ -797,8 +808,10 @@ hipError_t launch_mx_dequant(const uint8_t *q, const uint8_t *scale, int64_t row
                              int axis, uint16_t *out, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSeg - 1) / kSeg;
-    const int64_t tiles = nseg * ((rows + kRowsDq - 1) / kRowsDq);
-    if (tiles <= 0) return hipSuccess;
+    if (nseg <= 0 || rows <= 0) return hipSuccess;
+    // axis 0: column groups per XCD (the kernel's order); axis 1: plain
+    const int64_t tiles = axis == 0 ? xcd_row_grid(nseg * (32 / kRowsDq), (rows + 31) / 32)
+                                    : nseg * ((rows + kRowsDq - 1) / kRowsDq);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);
     if (axis == 1)
