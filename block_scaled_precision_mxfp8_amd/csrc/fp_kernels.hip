@@ -254,9 +254,15 @@ __global__ __launch_bounds__(256) void bfp8_1x128_kernel(const uint16_t *__restr
                                                          uint16_t *__restrict__ fq, int64_t tc,
                                                          int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg;
-    const int64_t rb = tile / nseg;
+    // with scales to write, a row block's segments run on one XCD, so each
+    // row's scale line fills inside one L2 (no barriers below)
+    int64_t seg, rb;
+    if (kQ) {
+        if (!xcd_row_tile(nseg, (rows + kRowsBq - 1) / kRowsBq, seg, rb)) return;
+    } else {
+        seg = blockIdx.x % nseg;
+        rb = blockIdx.x / nseg;
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
@@ -310,9 +316,10 @@ __global__ __launch_bounds__(256) void bfp8_to_mx_kernel(const uint8_t *__restri
                                                          uint8_t *__restrict__ s8, int64_t tc,
                                                          int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg;
-    const int64_t rb = tile / nseg;
+    // a row block's segments run on one XCD, so each row's scale line fills
+    // inside one L2 (no barriers below)
+    int64_t seg, rb;
+    if (!xcd_row_tile(nseg, (rows + kRowsDq - 1) / kRowsDq, seg, rb)) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
@@ -740,8 +747,9 @@ hipError_t launch_bfp8_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint
 {
     const int64_t tc = (cols + kBlk - 1) / kBlk;
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsBq - 1) / kRowsBq);
-    if (tiles <= 0) return hipSuccess;
+    const int64_t nrb = (rows + kRowsBq - 1) / kRowsBq;
+    if (nseg <= 0 || nrb <= 0) return hipSuccess;
+    const int64_t tiles = q ? xcd_row_grid(nseg, nrb) : nseg * nrb;  // the kernel's order
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);
     if (q && fq)
@@ -761,8 +769,9 @@ hipError_t launch_bfp8_to_mx(const uint8_t *q, const float *scale, int64_t rows,
 {
     const int64_t tc = (cols + kBlk - 1) / kBlk;
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsDq - 1) / kRowsDq);
-    if (tiles <= 0) return hipSuccess;
+    const int64_t nrb = (rows + kRowsDq - 1) / kRowsDq;
+    if (nseg <= 0 || nrb <= 0) return hipSuccess;
+    const int64_t tiles = xcd_row_grid(nseg, nrb);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bfp8_to_mx_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, scale,
                        rows, cols, q8, s8, tc, nseg);
