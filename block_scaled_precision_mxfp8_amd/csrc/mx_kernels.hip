@@ -124,9 +124,16 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
                                                          uint16_t *__restrict__ fq, int64_t ldf,
                                                          int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    mx_row_tile<kQ, kFQ, kRowsRow>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, tile % nseg,
-                                   tile / nseg);
+    // quantize-only: a row block's segments run on one XCD, so each row's
+    // scale line fills inside one L2 (as the MXFP4 quantizer does)
+    int64_t seg, rb;
+    if (kQ && !kFQ) {
+        if (!xcd_row_tile(nseg, (rows + kRowsRow - 1) / kRowsRow, seg, rb)) return;
+    } else {
+        seg = blockIdx.x % nseg;
+        rb = blockIdx.x / nseg;
+    }
+    mx_row_tile<kQ, kFQ, kRowsRow>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, seg, rb);
 }
 
 // ---------------------------------------------------------------------------
@@ -721,8 +728,9 @@ hipError_t launch_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int6
                              int64_t ldf, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSeg - 1) / kSeg;
-    const int64_t tiles = nseg * ((rows + kRowsRow - 1) / kRowsRow);
-    if (tiles <= 0) return hipSuccess;
+    const int64_t nrb = (rows + kRowsRow - 1) / kRowsRow;
+    if (nseg <= 0 || nrb <= 0) return hipSuccess;
+    const int64_t tiles = (q && !fq) ? xcd_row_grid(nseg, nrb) : nseg * nrb;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);
     if (q && fq)
