@@ -192,7 +192,7 @@ def main():
     traffic = read_traffic("act_16384")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "mx_colwise_kernel<col,row,fq>", "algorithmic_bytes": step_bytes,
+                "kernel": "mx_colwise_kernel<true,true,true,false,8>", "algorithmic_bytes": step_bytes,
                 "avg_launch_us": round(kern_ms * 1e3, 2),
                 "per_launch_us_min_max": [round(min(durs) * 1e3, 2), round(max(durs) * 1e3, 2)]}
     log(f"main: {value:.1f} GB/s per step, kernel {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")

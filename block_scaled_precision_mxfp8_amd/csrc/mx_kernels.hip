@@ -487,7 +487,8 @@ __global__ __launch_bounds__(64 * kW) void mx_colwise_kernel(
 // ---------------------------------------------------------------------------
 // Column-wise in the transposed layout (+ optional row-wise and fake-quant),
 // one read of x.  The four waves of a workgroup quantize 128 rows x 512
-// columns as above, staging the column codes and scales in LDS; after a
+// columns (mx_colwise_t_body, one 32-row group each), staging the column
+// codes and scales in LDS; after a
 // barrier the workgroup writes them out: column c's 128 codes are 128
 // contiguous bytes of qt (8 lanes, 16-byte stores) and its 4 scales one
 // dword of st.  Measured on MI355X against alternatives (cold [16384, 7168]
