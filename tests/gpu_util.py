@@ -1,9 +1,23 @@
 """Helpers for the GPU parity tests: moving bf16 bit patterns between numpy
 (oracle side) and torch device tensors (HIP side), and byte-exact compares."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
+
+# Host threads for oracle work in the full-size tests.  The oracle's C calls
+# release the GIL, so tensors run in parallel; 16 is the host CPU share a GPU
+# box grants one GPU, whatever os.cpu_count() reports there.
+HOST_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def parallel_map(fn, items, workers: int = HOST_THREADS):
+    """[fn(item) for item in items] over a thread pool, in order; the first
+    exception raised by any call is re-raised."""
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
 
 
 def to_dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:

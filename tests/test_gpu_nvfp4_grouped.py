@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import announce, assert_same, f32bits, to_dev_bf16, u8
+from gpu_util import announce, assert_same, bits16, f32bits, parallel_map, to_dev_bf16, u8
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,40 @@ def test_grouped_full_size_experts(gpu, orc):
     """Four experts' gate and up at full size [2048, 7168], shared scales."""
     xs = experts(4, 2048, 7168, 400)
     check_grouped(gpu, orc, xs, [i // 2 for i in range(len(xs))], 4, "full-size")
+
+
+@pytest.mark.timeout(900)
+def test_grouped_moe_gate_up_full(gpu, orc):
+    """The benchmarked launch: the gate and up weights of all 128 MoE experts
+    ([2048, 7168] each, drawn as the moe_experts workload draws them) in one
+    grouped call, gate and up of an expert sharing one global scale.  Every
+    expert's g and every tensor's codes and scales against the oracle, which
+    runs expert by expert (a scale group depends on its members only) over
+    host threads."""
+    shapes = workloads.moe_shapes()
+    mult = workloads.moe_multipliers()
+    gu = [i for i, (name, _, _) in enumerate(shapes)
+          if name.endswith(("gate_proj.weight", "up_proj.weight"))]
+    n_exp = len(shapes) // 3
+    assert len(gu) == 2 * n_exp
+    announce(f"nvfp4 grouped moe gate/up: {len(gu)} tensors, {n_exp} groups")
+    xs = [workloads.moe_tensor(i, shapes[i][1], shapes[i][2], mult[i // 3], "cuda") for i in gu]
+    outs, gs = gpu.nvfp4_quantize_grouped(xs, [i // 3 for i in gu], n_exp)
+    torch.cuda.synchronize()
+    g_got = f32bits(gs)
+    announce("nvfp4 grouped moe gate/up: oracle per expert")
+
+    def check(e):
+        k0, k1 = 2 * e, 2 * e + 1            # gate and up of expert e in xs
+        assert gu[k0] // 3 == e and gu[k1] // 3 == e
+        oouts, og = orc.nvfp4_quantize_grouped([bits16(xs[k0]), bits16(xs[k1])], [0, 0], 1)
+        assert_same(f"expert {e} g", g_got[e:e + 1], f32bits(og))
+        for k, (oq, os_) in zip((k0, k1), oouts):
+            assert_same(f"expert {e} q[{k}]", u8(outs[k][0]), oq)
+            assert_same(f"expert {e} s[{k}]", u8(outs[k][1]), os_)
+        return e
+
+    assert parallel_map(check, range(n_exp)) == list(range(n_exp))
 
 
 def test_grouped_workspace_needs_no_initial_contents(gpu, orc):
