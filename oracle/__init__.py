@@ -76,6 +76,10 @@ class Oracle:
         L.orc_e2m1_to_double.restype = ctypes.c_double
         L.orc_double_to_e2m1.argtypes = [ctypes.c_double]
         L.orc_double_to_e2m1.restype = ctypes.c_uint8
+        for nm, outp in (("orc_f32_bits_to_e4m3", _u8p), ("orc_f32_bits_to_e2m1", _u8p),
+                         ("orc_f32_bits_to_bf16", _u16p)):
+            getattr(L, nm).argtypes = [ctypes.c_uint32, _i64, ctypes.c_uint32, outp]
+            getattr(L, nm).restype = None
         L.orc_mxfp8_quantize_rowwise.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
         L.orc_mxfp8_quantize_rowwise.restype = None
         L.orc_mxfp8_quantize_padcrop.argtypes = [_u16p, _i64, _i64, _u8p, _u8p]
@@ -125,6 +129,19 @@ class Oracle:
         L.orc_nvfp4_dequantize.restype = None
         self.L = L
         self.path = path
+
+    # ---- element encoders over runs of fp32 bit patterns -------------------
+    def f32_bits_to(self, fmt: str, first: int, n: int, stride: int = 1, out=None) -> np.ndarray:
+        """Encodings (fmt 'e4m3', 'e2m1' or 'bf16') of the fp32 values with
+        bit patterns first + i * stride, i < n, into out (or a new array)."""
+        dt = np.uint16 if fmt == "bf16" else np.uint8
+        if out is None:
+            out = np.empty((n,), dt)
+        assert out.dtype == dt and out.size >= n and out.flags["C_CONTIGUOUS"]
+        assert 0 <= first and first + (n - 1) * stride <= 0xFFFFFFFF
+        fn = getattr(self.L, f"orc_f32_bits_to_{fmt}")
+        fn(int(first), int(n), int(stride), _p(out, _u16p if fmt == "bf16" else _u8p))
+        return out
 
     # ---- scalar codecs ----------------------------------------------------
     def bf16_to_double(self, b: int) -> float:

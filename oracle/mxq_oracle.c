@@ -180,6 +180,41 @@ uint8_t orc_double_to_e2m1(double v)
     return sign | (uint8_t)(((Er + 1) << 1) | frac);
 }
 
+/* The element encoders over runs of fp32 bit patterns, for the exhaustive
+ * sweeps of the library's fp32 -> E4M3 / E2M1 / bf16 converters: out[i] is
+ * the encoding of the fp32 value whose bit pattern is first + i * stride
+ * (as a double, which holds every fp32 value exactly).  Plain loops over the
+ * scalar encoders above. */
+void orc_f32_bits_to_e4m3(uint32_t first, int64_t n, uint32_t stride, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = first + (uint32_t)i * stride;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        out[i] = orc_double_to_e4m3((double)f);
+    }
+}
+
+void orc_f32_bits_to_e2m1(uint32_t first, int64_t n, uint32_t stride, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = first + (uint32_t)i * stride;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        out[i] = orc_double_to_e2m1((double)f);
+    }
+}
+
+void orc_f32_bits_to_bf16(uint32_t first, int64_t n, uint32_t stride, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = first + (uint32_t)i * stride;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        out[i] = orc_double_to_bf16((double)f);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* MXFP8: groups of 32, one E8M0 scale, E4M3 elements                        */
 /* ------------------------------------------------------------------------ */
