@@ -37,7 +37,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxq.so")
 
-MXQ_OK, MXQ_EINVAL, MXQ_ESHAPE, MXQ_EALIGN, MXQ_EHIP, MXQ_ESIZE = range(6)
+MXQ_OK, MXQ_EINVAL, MXQ_ESHAPE, MXQ_EALIGN, MXQ_EHIP, MXQ_ESIZE, MXQ_ECAPTURE = range(7)
 MX_GROUP = 32
 NV_BLOCK = 16
 
@@ -52,6 +52,7 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "mxq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mxq_abi_version": (ctypes.c_int, []),
+    "mxq_build_id": (ctypes.c_char_p, []),
     "mxq_quantize_rowwise": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]),
     "mxq_quantize_colwise": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mxq_quantize_colwise_t": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
@@ -108,18 +109,30 @@ class MXQError(RuntimeError):
         super().__init__(f"{fn}: {status_string(status)} (status {status})")
 
 
+class StaleLibraryError(RuntimeError):
+    """libmxq.so was built from sources other than the ones beside it."""
+
+
 def load() -> ctypes.CDLL:
-    """Load libmxq.so (building it first only if it does not exist)."""
+    """Load libmxq.so, building it first only if it does not exist.  A library
+    whose build id (a hash of the sources, header and flags it was compiled
+    from) differs from the hash of the sources in this tree is refused: run
+    ``python -m block_scaled_precision_mxfp8_amd.build`` after editing them."""
     global _lib
     if _lib is None:
+        from . import build as _build
         if not os.path.exists(LIB_PATH):
-            from . import build as _build
             _build.build()
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        built, here = L.mxq_build_id().decode(), _build.source_hash()
+        if built != here:
+            raise StaleLibraryError(
+                f"{LIB_PATH} was built from other sources (build id {built}, sources {here}); "
+                f"rebuild it with `python -m block_scaled_precision_mxfp8_amd.build`")
         _lib = L
     return _lib
 

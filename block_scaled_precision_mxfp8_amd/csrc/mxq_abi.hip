@@ -30,6 +30,18 @@ inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s);
 
 inline mxq_status from_hip(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_EHIP; }
 
+// MXQ_ECAPTURE while `stream` is being captured into a graph.  The one-call
+// grouped forms copy their launch table from a host buffer that is freed when
+// the call returns; a captured copy node would read that freed memory on every
+// replay.  (A query the runtime refuses, e.g. of the legacy stream during
+// another stream's global-mode capture, also refuses the call.)
+inline mxq_status refuse_capture(hipStream_t stream)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MXQ_EHIP;
+    return cs == hipStreamCaptureStatusNone ? MXQ_OK : MXQ_ECAPTURE;
+}
+
 mxq_status check_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
                          const uint8_t *q, int64_t ldq, const uint8_t *scale, int64_t lds,
                          const uint16_t *fq, int64_t ldf, bool need_q)
@@ -227,11 +239,18 @@ const char *mxq_status_string(int status)
     case MXQ_EALIGN: return "misaligned pointer or leading dimension";
     case MXQ_EHIP: return "HIP runtime error at launch";
     case MXQ_ESIZE: return "workspace too small or size overflow";
+    case MXQ_ECAPTURE:
+        return "stream is being captured: this call copies from host memory (capture the plan form)";
     default: return "unknown status";
     }
 }
 
 int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+#ifndef MXQ_BUILD_ID
+#define MXQ_BUILD_ID "unidentified"  // built without the package's build script
+#endif
+const char *mxq_build_id(void) { return MXQ_BUILD_ID; }
 
 mxq_status mxq_quantize_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
                                 uint8_t *q, int64_t ldq, uint8_t *scale, int64_t lds,
@@ -373,7 +392,9 @@ mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n, 
     mxq_grouped_plan plan;
     mxq_status st = mx_build(descs, n, img, plan);
     if (st != MXQ_OK || plan.n_entries == 0) return st;
-    // pageable source: the copy has consumed it by the time hipMemcpyAsync returns
+    st = refuse_capture(as_stream(stream));
+    if (st != MXQ_OK) return st;
+    // pageable source: the copy has read it by the time hipMemcpyAsync returns
     if (hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice,
                        as_stream(stream)) != hipSuccess)
         return MXQ_EHIP;
@@ -549,7 +570,9 @@ mxq_status nvfp4_quantize_grouped(const nvfp4_group_desc *descs, int32_t n, floa
     if (!workspace) return MXQ_EINVAL;
     if (!aligned(workspace, 16)) return MXQ_EALIGN;
     if (workspace_bytes < nvfp4_grouped_workspace_size(descs, n)) return MXQ_ESIZE;
-    // pageable source: the copy has consumed it by the time it returns
+    st = refuse_capture(as_stream(stream));
+    if (st != MXQ_OK) return st;
+    // pageable source: the copy has read it by the time it returns
     if (!img.empty() && hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice,
                                        as_stream(stream)) != hipSuccess)
         return MXQ_EHIP;

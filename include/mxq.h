@@ -27,6 +27,10 @@
  *   - Data pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates, frees or synchronizes; every call is asynchronous on
  *     `stream` (a hipStream_t passed as void*, NULL = the default stream).
+ *     The two one-call grouped forms are the exception: they copy a launch
+ *     table from host memory, which may block the host until the copy has
+ *     read it, and they refuse to run while `stream` is being captured
+ *     (their prepared-plan forms do neither).
  *   - bf16 tensors are passed as uint16_t bit patterns; E4M3, E8M0 and packed
  *     E2M1 codes as uint8_t; fp32 scales as float.  All are row-major.
  *   - Arguments are checked on the host before anything is launched; a
@@ -52,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 1
+#define MXQ_ABI_VERSION 2
 
 typedef enum mxq_status {
     MXQ_OK = 0,
@@ -60,7 +64,9 @@ typedef enum mxq_status {
     MXQ_ESHAPE = 2, /* shape the operation does not accept (e.g. cols % 32 != 0) */
     MXQ_EALIGN = 3, /* pointer or leading dimension misaligned for vector access */
     MXQ_EHIP = 4,   /* the HIP runtime rejected a launch or copy */
-    MXQ_ESIZE = 5   /* workspace too small, or a size overflows the index type */
+    MXQ_ESIZE = 5,  /* workspace too small, or a size overflows the index type */
+    MXQ_ECAPTURE = 6 /* a call that copies from host memory, made while `stream`
+                        is being captured into a graph (use the plan form) */
 } mxq_status;
 
 /* Static English text for a status code (never NULL). */
@@ -68,6 +74,12 @@ const char *mxq_status_string(int status);
 
 /* MXQ_ABI_VERSION of the built library. */
 int mxq_abi_version(void);
+
+/* Identifier of the sources the library was built from: the first 16 hex
+ * digits of a sha256 over the compiler flags and every source and header
+ * file.  A loader compares it with the same hash of the tree it ships with
+ * and refuses a library built from other sources. */
+const char *mxq_build_id(void);
 
 /*
  * Row-wise MXFP8 quantization ("PR #1935 完整报告", 实现拆解 item 1).
@@ -174,11 +186,15 @@ size_t mxq_grouped_workspace_size(int32_t n);
  *   descs      HOST array of n descriptors (read during the call only)
  *   workspace  DEVICE buffer of >= mxq_grouped_workspace_size(n) bytes,
  *              16-byte aligned; the library stages a launch table there with
- *              an async host-to-device copy on `stream`, so the buffer must
- *              not be reused until the launch has finished
+ *              a host-to-device copy on `stream` from a host buffer that
+ *              lives only during the call (so the call may block the host
+ *              until the copy has read it), and the buffer must not be
+ *              reused until the launch has finished
  * Returns MXQ_EINVAL for n < 0 or NULL pointers, MXQ_ESIZE for a small
- * workspace, else the first failing descriptor's status.  n == 0 launches
- * nothing.
+ * workspace, else the first failing descriptor's status; MXQ_ECAPTURE, with
+ * nothing enqueued, while `stream` is being captured (a captured copy would
+ * read the freed host buffer on replay: capture the plan form instead).
+ * n == 0 launches nothing.
  */
 mxq_status mxq_quantize_rowwise_grouped(const mxq_group_desc *descs, int32_t n,
                                         void *workspace, size_t workspace_bytes, void *stream);
@@ -335,7 +351,11 @@ mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t
  *                  memory, 16-byte aligned, caller-owned: the launch table and
  *                  one amax partial per 512 x 32 tile (no initial contents
  *                  needed; calls that overlap on one workspace race).  It is
- *                  filled by an asynchronous copy on `stream`.
+ *                  filled by a host-to-device copy on `stream` from a host
+ *                  buffer that lives only during the call, so the call may
+ *                  block the host until the copy has read it, and it returns
+ *                  MXQ_ECAPTURE, with nothing enqueued, while `stream` is
+ *                  being captured (capture the plan form instead).
  */
 typedef struct nvfp4_group_desc {
     const uint16_t *x;

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -52,10 +53,53 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.mxq_abi_version() == 1
-    for st in range(6):
+    assert lib.mxq_abi_version() == 2
+    for st in range(7):
         assert lib.mxq_status_string(st)
     assert b"unknown" in lib.mxq_status_string(99)
+    assert b"captur" in lib.mxq_status_string(mxq.MXQ_ECAPTURE)
+
+
+def test_build_id_matches_sources(lib):
+    """The library in the tree was built from the sources beside it."""
+    from block_scaled_precision_mxfp8_amd import build
+    assert lib.mxq_build_id().decode() == build.source_hash()
+
+
+def _load_copy(root):
+    code = ("import block_scaled_precision_mxfp8_amd as m\n"
+            "try:\n    m.load()\nexcept m.StaleLibraryError as e:\n"
+            "    print('STALE', e)\nelse:\n    print('LOADED')\n")
+    env = dict(os.environ, PYTHONPATH=str(root))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    return r.stdout
+
+
+def test_stale_library_is_refused(tmp_path):
+    """A copy of the package with its built library loads; after an edit to a
+    kernel source, or to the public header, the same library is refused
+    (StaleLibraryError names the rebuild), and nothing is rebuilt behind the
+    caller's back."""
+    import shutil
+    pkg = tmp_path / "block_scaled_precision_mxfp8_amd"
+    shutil.copytree(os.path.dirname(mxq.__file__), pkg,
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    lib_before = (pkg / "libmxq.so").read_bytes()
+    assert "LOADED" in _load_copy(tmp_path)
+    src = pkg / "csrc" / "mx_kernels.hip"
+    text = src.read_text()
+    src.write_text(text + "\n// an edit after the build\n")
+    out = _load_copy(tmp_path)
+    assert "STALE" in out and "rebuild" in out
+    src.write_text(text)
+    assert "LOADED" in _load_copy(tmp_path)
+    hdr = tmp_path / "include" / "mxq.h"
+    hdr.write_text(hdr.read_text().replace("MXQ_ABI_VERSION 2", "MXQ_ABI_VERSION 3"))
+    assert "STALE" in _load_copy(tmp_path)
+    assert (pkg / "libmxq.so").read_bytes() == lib_before
 
 
 P16 = ctypes.c_void_p(0x10000)   # aligned fake device addresses: never dereferenced,

@@ -145,3 +145,37 @@ def test_prepared_grouped_in_a_graph(gpu, orc):
         torch.cuda.synchronize()
         _check_mx(orc, mb, mx_prep.outputs, f"graph replay {k} MXFP8")
         _check_nv(orc, nb, nv_prep.outputs, nv_prep.global_scales, f"graph replay {k} NVFP4")
+
+
+def test_one_call_grouped_forms_refuse_capture(gpu, orc):
+    """The one-call grouped forms copy their launch table from a host buffer
+    that is freed when they return, so under stream capture they refuse with
+    MXQ_ECAPTURE and enqueue nothing; the capture ends cleanly, its (empty)
+    graph is never replayed, and the same calls then run eagerly and match the
+    oracle."""
+    import block_scaled_precision_mxfp8_amd as mxq
+    xs_b = _mx_inputs(1700)
+    xs = [to_dev_bf16(b) for b in xs_b]
+    nv_b = _nv_inputs(1800)
+    nv = [to_dev_bf16(b) for b in nv_b]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    announce("one-call grouped forms under capture")
+    with torch.cuda.stream(side):
+        g.capture_begin()
+        try:
+            with pytest.raises(mxq.MXQError) as e1:
+                gpu.quantize_rowwise_grouped(xs)
+            with pytest.raises(mxq.MXQError) as e2:
+                gpu.nvfp4_quantize_grouped(nv, NV_GROUPS, NV_N_GROUPS)
+        finally:
+            g.capture_end()
+    assert e1.value.status == mxq.MXQ_ECAPTURE and "plan form" in str(e1.value)
+    assert e2.value.status == mxq.MXQ_ECAPTURE
+    torch.cuda.synchronize()
+    announce("one-call grouped forms eagerly after the refused capture")
+    _check_mx(orc, xs_b, gpu.quantize_rowwise_grouped(xs), "eager mx")
+    outs, gs = gpu.nvfp4_quantize_grouped(nv, NV_GROUPS, NV_N_GROUPS)
+    torch.cuda.synchronize()
+    _check_nv(orc, nv_b, outs, gs, "eager nv")
