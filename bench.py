@@ -18,13 +18,19 @@ dequantization, gets more copies).
 
 Besides the timed steps it reports, in the same line:
   roofline      the one-pass kernel's achieved GB/s (HIP events on the stream
-                it runs on) against MI355X's 8 TB/s HBM peak, plus HBM traffic
+                it runs on) against MI355X's 8 TB/s HBM peak and against the
+                streaming ceiling of its own read:write mix, plus HBM traffic
                 from the committed rocprofv3 counter summary when it still
                 matches the kernel source
+  ceilings      per read:write mix (read, write, copy, row-wise quantize,
+                one-pass), the best rate of several trivial-arithmetic
+                streaming patterns (bench_streams.hip) over the same cold
+                batches; ceiling_runs lists every pattern's rate
   cpu_baseline  the CPU oracle (single-threaded C) timed on a bounded sample
                 of the same workload, and the same sharded over host threads
   breakdown     every other quantizer workload (row-wise weight, grouped MoE
-                experts, block-FP8, NVFP4, dequantizers), each timed on its own
+                experts, block-FP8, NVFP4, dequantizers), each timed on its own;
+                the MXFP8 quantizers also as a fraction of their mix's ceiling
 """
 from __future__ import annotations
 
@@ -50,8 +56,51 @@ KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_mxfp8_amd", "csrc",
                   for f in ("mx_kernels.hip", "mxq_device.hpp")]
 
 
+STREAMS_SRC = os.path.join(ROOT, "bench_streams.hip")
+STREAMS_LIB = os.path.join(ROOT, "libbench_streams.so")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def streams_hash() -> str:
+    """Hash of the streaming-ceiling kernels' sources and flags."""
+    from block_scaled_precision_mxfp8_amd import build as pb
+    h = hashlib.sha256(" ".join(pb.HIPFLAGS).encode())
+    for p in (STREAMS_SRC, os.path.join(pb.CSRC, "mxq_device.hpp")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def build_streams() -> str:
+    """Compile bench_streams.hip (the streaming-ceiling kernels) for gfx950."""
+    import subprocess
+    from block_scaled_precision_mxfp8_amd import build as pb
+    tmp = STREAMS_LIB + ".tmp"
+    subprocess.run([pb.HIPCC, *pb.HIPFLAGS, "-shared", f"-DSTREAMS_BUILD_ID=\"{streams_hash()}\"",
+                    "-I", pb.CSRC, STREAMS_SRC, "-o", tmp], check=True)
+    os.replace(tmp, STREAMS_LIB)
+    return STREAMS_LIB
+
+
+def load_streams():
+    """The streaming-ceiling library (built first if missing; a build from
+    other sources is refused)."""
+    if not os.path.exists(STREAMS_LIB):
+        build_streams()
+    L = ctypes.CDLL(STREAMS_LIB)
+    L.bench_streams_build_id.restype = ctypes.c_char_p
+    if L.bench_streams_build_id().decode() != streams_hash():
+        raise RuntimeError(f"{STREAMS_LIB} was built from other sources: run "
+                           f"__graft_entry__.build()")
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.bench_stream_tiled.restype = ctypes.c_int
+    L.bench_stream_tiled.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.bench_stream_flat.restype = ctypes.c_int
+    L.bench_stream_flat.argtypes = [ctypes.c_int, vp, i64, vp, vp, vp, vp, ctypes.c_int, vp]
+    return L
 
 
 def kernel_source_hash() -> str:
@@ -82,6 +131,63 @@ def read_traffic(workload: str):
                     return None
                 return float(kv["bytes"])
     return None
+
+
+MIX_BYTES = {  # bytes moved per element by each streaming-ceiling mix (tiled / flat)
+    "read": (2.0, 2.0), "write": (2.0, 2.0), "copy": (4.0, 4.0),
+    "row": (3.0 + 1 / 32, 3.0), "onepass": (6.0 + 1 / 32, 6.0)}
+MIXES = ["read", "write", "copy", "row", "onepass"]   # tiled variant order
+FLAT_MODES = ["read", "copy", "row", "onepass", "write"]
+
+
+def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
+    """Best GB/s per mix over the tiled (R = 1, 2, 4, 8 rows per wave) and flat
+    (U = 2, 4, 8 loads in flight; 1024, 2048, 4096 workgroups) patterns, each
+    timed like the quantizers: back-to-back launches cycling over the cold
+    batches after an untimed warm-up."""
+    import torch
+    e = rows * cols
+    sink = torch.empty((16,), dtype=torch.int32, device=batches[0]["x"].device)
+
+    def P(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    def timed(launch):
+        for i in range(max(16, len(batches))):
+            launch(batches[i % len(batches)])
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(iters):
+            launch(batches[i % len(batches)])
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / iters * 1e-3
+
+    runs = {}
+    for v in range(20):
+        mix, R = MIXES[v // 4], 1 << (v % 4)
+
+        def go(d, v=v):
+            st = L.bench_stream_tiled(v, P(d["x"]), rows, cols, P(d["qc"]), P(d["qr"]), P(d["fq"]),
+                                      P(d["sr"]), P(sink), sp)
+            if st != 0:
+                raise RuntimeError(f"bench_stream_tiled({v}) status {st}")
+        runs[f"{mix} tiled R{R}"] = (mix, MIX_BYTES[mix][0] * e / timed(go) / 1e9)
+    for v in range(15):
+        mix, U = FLAT_MODES[v // 3], (2, 4, 8)[v % 3]
+        for grid in (1024, 2048, 4096):
+            def go(d, v=v, grid=grid):
+                st = L.bench_stream_flat(v, P(d["x"]), e // 8, P(d["qc"]), P(d["qr"]), P(d["fq"]),
+                                         P(sink), grid, sp)
+                if st != 0:
+                    raise RuntimeError(f"bench_stream_flat({v}) status {st}")
+            runs[f"{mix} flat U{U} grid{grid}"] = (mix, MIX_BYTES[mix][1] * e / timed(go) / 1e9)
+    best = {}
+    for name, (mix, gbs) in runs.items():
+        if mix not in best or gbs > best[mix]["GB/s"]:
+            best[mix] = {"GB/s": round(gbs, 1), "pattern": name}
+    return best, {k: round(g, 1) for k, (_, g) in runs.items()}
 
 
 def main():
@@ -197,22 +303,16 @@ def main():
                 "per_launch_us_min_max": [round(min(durs) * 1e3, 2), round(max(durs) * 1e3, 2)]}
     log(f"main: {value:.1f} GB/s per step, kernel {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
 
-    # plain device copy of the same byte count, cycled the same way: the
-    # practical ceiling of a read/write stream
-    half = step_bytes // 2
-    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev),
-              torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(BATCHES)]
-    for i in range(BATCHES):
-        pairs[i][1].copy_(pairs[i][0])
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for i in range(20):
-        pairs[i % BATCHES][1].copy_(pairs[i % BATCHES][0])
-    b.record(stream)
-    b.synchronize()
-    copy_gbs = 2 * half / (a.elapsed_time(b) / 20 * 1e-3) / 1e9
-    del pairs
+    # Streaming ceilings: per read:write mix, the best of several access
+    # patterns with trivial arithmetic (bench_streams.hip), over the same cold
+    # batches.  The quantizer kernels are reported against the ceiling of
+    # their own mix as well as against the 8 TB/s peak.
+    ceilings, ceiling_runs = measure_ceilings(load_streams(), batches, rows, cols, stream, sp)
+    oc = ceilings["onepass"]
+    roofline["ceiling"] = {"mix": "onepass (2 B read : 4 + 1/16 B written per element)",
+                           "GB/s": oc["GB/s"], "pattern": oc["pattern"],
+                           "frac": round(achieved / oc["GB/s"], 4)}
+    log("ceilings: " + ", ".join(f"{k} {v['GB/s']:.0f} ({v['pattern']})" for k, v in ceilings.items()))
 
     # ------------------------------------------------------------------
     # CPU oracle on a bounded sample (first cpu_rows rows, same arithmetic)
@@ -270,12 +370,13 @@ def main():
     # ------------------------------------------------------------------
     breakdown = {}
     if not args.no_breakdown:
-        def rotated(launches, nbytes, iters=20):
+        def rotated(launches, nbytes, iters=20, mix=None):
             """Back-to-back launches cycling through copies with their own
             buffers; per-launch time = total / iters.  The untimed warm-up
             touches every copy and runs at least 16 launches, so that the
             first workload after the CPU baseline is not timed while the GPU
-            is still leaving its idle clocks."""
+            is still leaving its idle clocks.  With `mix`, the result also
+            gives the fraction of that mix's streaming ceiling."""
             for i in range(max(len(launches), 16)):
                 launches[i % len(launches)]()
             torch.cuda.synchronize()
@@ -287,9 +388,13 @@ def main():
             b.synchronize()
             ms = a.elapsed_time(b) / iters
             gbs = nbytes / (ms * 1e-3) / 1e9
-            return {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(nbytes),
-                    "copies": len(launches)}
+            r = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "bytes": int(nbytes),
+                 "copies": len(launches)}
+            if mix is not None:
+                r["ceiling_mix"] = mix
+                r["frac_ceiling"] = round(gbs / ceilings[mix]["GB/s"], 4)
+            return r
 
         def ncopies(in_bytes):
             """Copies of a workload whose launch reads in_bytes, so that
@@ -301,14 +406,16 @@ def main():
         breakdown["act_16384 row-wise only"] = rotated(
             [lambda d=d: check(lib.mxq_quantize_rowwise(P(d["x"]), rows, cols, cols, P(d["qr"]),
                                                         cols, P(d["sr"]), cols // 32, None, 0, sp),
-                               "rowwise") for d in batches], rb)
+                               "rowwise") for d in batches], rb, mix="row")
         breakdown["act_16384 column-wise only"] = rotated(
             [lambda d=d: check(lib.mxq_quantize_colwise(P(d["x"]), rows, cols, P(d["qc"]),
                                                         P(d["sc"]), None, None, None, sp),
-                               "colwise") for d in batches], 2 * e + e + batches[0]["sc"].numel())
+                               "colwise") for d in batches], 2 * e + e + batches[0]["sc"].numel(),
+            mix="row")
         breakdown["act_16384 fake-quant only"] = rotated(
             [lambda d=d: check(lib.mxq_fake_quant(P(d["x"]), rows, cols, 1, P(d["fq"]), sp),
-                               "fake_quant") for d in batches], 4 * e)
+                               "fake_quant") for d in batches], 4 * e, mix="copy")
+
         def code_copies(qk, sk):
             """Copies of the batches' codes and scales for a dequantization
             (its input is half or less of a batch's), each with its own output."""
@@ -408,7 +515,7 @@ def main():
         ge = sum(r * c for (_, r, c) in shapes)
         breakdown["moe_experts grouped row-wise"] = rotated(
             [lambda: check(lib.mxq_quantize_rowwise_grouped(descs, len(xs), P(gws), wsz, sp),
-                           "grouped")], 3 * ge + ge // 32, iters=10)
+                           "grouped")], 3 * ge + ge // 32, iters=10, mix="row")
         del outs, gws
         torch.cuda.empty_cache()
         # NVFP4 of the 256 gate/up tensors in one grouped call, gate and up of
@@ -502,7 +609,8 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "copy_ceiling_GBs": round(copy_gbs, 1),
+        "ceilings": ceilings,
+        "ceiling_runs": ceiling_runs,
         "breakdown": breakdown,
         "device": torch.cuda.get_device_name(dev),
     }
