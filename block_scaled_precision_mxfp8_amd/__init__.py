@@ -20,6 +20,7 @@ Entry points (names follow the C ABI):
           blockfp8_quantize_1x128 / blockfp8_dequantize_1x128 / fp8_simulate_qat
           blockfp8_to_mxfp8(q, S)                              FP8 -> BF16 -> MXFP8
   NVFP4   nvfp4_quantize(x) / nvfp4_dequantize(q, s, g),
+          nvfp4_quantize_noalloc(x)                            no workspace
           nvfp4_quantize_grouped(xs, groups, n_groups)         shared global scales
           prepare_nvfp4_grouped(xs, groups, n_groups).run()    table built once
 and the adapter-level helpers of the MXFP8 export path ("PR #1935 完整报告",
@@ -74,6 +75,7 @@ SIGNATURES = {
     "mxfp4_fake_quant": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "nvfp4_workspace_size": (_sz, []),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_quantize_noalloc": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp]),
     "nvfp4_grouped_workspace_size": (_sz, [_vp, _i32]),
     "nvfp4_quantize_grouped": (ctypes.c_int, [_vp, _i32, _vp, _i32, _vp, _sz, _vp]),
@@ -553,6 +555,21 @@ def nvfp4_quantize(x: torch.Tensor, workspace: torch.Tensor | None = None):
     st = load().nvfp4_quantize(_ptr(x), rows, cols, _ptr(q), _ptr(s), _ptr(g), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(x))
     _check("nvfp4_quantize", st)
+    return q, s, g
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor):
+    """nvfp4_quantize with the amax partials in the library's own per-GPU
+    array instead of a workspace (calls that overlap on one GPU race)."""
+    _need_bf16_cuda(x)
+    x = x.contiguous()
+    rows, cols = x.shape
+    dev = x.device
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((rows, cols // NV_BLOCK), dtype=torch.uint8, device=dev)
+    g = torch.empty((1,), dtype=torch.float32, device=dev)
+    st = load().nvfp4_quantize_noalloc(_ptr(x), rows, cols, _ptr(q), _ptr(s), _ptr(g), _stream(x))
+    _check("nvfp4_quantize_noalloc", st)
     return q, s, g
 
 

@@ -17,6 +17,8 @@
 // (div_markstein); no fast-math, denormals kept.
 #include <math.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "mxq_device.hpp"
 
@@ -779,12 +781,14 @@ hipError_t launch_bfp8_to_mx(const uint8_t *q, const float *scale, int64_t rows,
 }
 
 hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
-                              uint8_t *s, float *g, uint32_t *ws, hipStream_t stream)
+                              uint8_t *s, float *g, uint32_t *ws, int64_t ws_words,
+                              hipStream_t stream)
 {
     const int64_t nvec = rows * cols / 8;
     if (nvec <= 0) return hipSuccess;
     const int64_t want = (nvec + 255) / 256;
     const int ablocks = (int)(want < kNvAmaxBlocks ? want : kNvAmaxBlocks);
+    if (ablocks > ws_words) return hipErrorInvalidValue;  // one partial per amax workgroup
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
     const int64_t tiles = nseg * ((rows + kRowsNvQ - 1) / kRowsNvQ);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -797,6 +801,62 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,
                        cols, q, s, g, nseg);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 for callers that cannot allocate: the amax partials go to `scratch`,
+// a fixed array of this library (kNvAmaxBlocks words, 4 KiB) that each GPU
+// holds until the process ends, instead of a caller workspace.  In host code
+// `scratch` names a host-side stand-in, not device memory: its address on a
+// device comes from hipGetSymbolAddress, resolved once per device with that
+// device current and kept below.  Every call on a GPU shares that GPU's
+// array, so calls that overlap on one GPU race.  Each call writes every
+// partial it later reads, so nothing needs clearing between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t scratch[kNvAmaxBlocks];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+uint32_t *scratch_on[kMaxDevices];  // device address of `scratch` per device, once resolved
+
+// The device address of `scratch` on the device that runs `stream`.
+hipError_t scratch_for(hipStream_t stream, uint32_t **out)
+{
+    int dev = -1;
+    hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_on[dev]) {
+        int cur = -1;
+        err = hipGetDevice(&cur);
+        if (err != hipSuccess) return err;
+        if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        scratch_on[dev] = static_cast<uint32_t *>(p);
+    }
+    *out = scratch_on[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_quant_noalloc(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                                      uint8_t *s, float *g, hipStream_t stream)
+{
+    uint32_t *ws = nullptr;
+    const hipError_t err = scratch_for(stream, &ws);
+    if (err != hipSuccess) return err;
+    return launch_nvfp4_quant(x, rows, cols, q, s, g, ws, kNvAmaxBlocks, stream);
 }
 
 int64_t nvfp4_tiles(int64_t rows, int64_t cols, int64_t *nseg)

@@ -64,8 +64,14 @@ hipError_t launch_bfp8_to_mx(const uint8_t *q, const float *scale, int64_t rows,
 // NVFP4 amax partials: at most this many workgroups write one word each.
 constexpr int kNvAmaxBlocks = 1024;
 
+// ws: ws_words words of amax partials (hipErrorInvalidValue when the amax
+// pass would need more; it needs at most kNvAmaxBlocks).
 hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
-                              uint8_t *s, float *g, uint32_t *ws, hipStream_t stream);
+                              uint8_t *s, float *g, uint32_t *ws, int64_t ws_words,
+                              hipStream_t stream);
+// The same with the partials in the library's own per-device array.
+hipError_t launch_nvfp4_quant_noalloc(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q,
+                                      uint8_t *s, float *g, hipStream_t stream);
 // Launch table entry of grouped NVFP4 (staged in the caller's workspace,
 // followed by int32 arrays of first tiles and scale groups, then one uint32
 // amax partial per tile).  Tiles: 512 columns x 32 rows.

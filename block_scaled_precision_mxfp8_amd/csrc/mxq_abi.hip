@@ -527,21 +527,44 @@ mxq_status blockfp8_to_mxfp8(const uint8_t *q, const float *scale, int64_t rows,
     return from_hip(mxq::launch_bfp8_to_mx(q, scale, rows, cols, q8, scale8, as_stream(stream)));
 }
 
-mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
-                          uint8_t *s_e4m3, float *global_scale, void *workspace,
-                          size_t workspace_bytes, void *stream)
+// Checks shared by the two single-tensor NVFP4 entry points.
+static mxq_status check_nvfp4(const uint16_t *x, int64_t rows, int64_t cols,
+                              const uint8_t *q_packed, const uint8_t *s_e4m3,
+                              const float *global_scale)
 {
     if (rows < 0 || cols < 0) return MXQ_EINVAL;
     if (cols % 16 != 0) return MXQ_ESHAPE;
     if (rows == 0 || cols == 0) return MXQ_OK;
-    if (!x || !q_packed || !s_e4m3 || !global_scale || !workspace) return MXQ_EINVAL;
-    if (workspace_bytes < nvfp4_workspace_size()) return MXQ_ESIZE;
-    if (!aligned(x, 16) || !aligned(q_packed, 4) || !aligned(global_scale, 4) ||
-        !aligned(workspace, 4))
-        return MXQ_EALIGN;
+    if (!x || !q_packed || !s_e4m3 || !global_scale) return MXQ_EINVAL;
+    if (!aligned(x, 16) || !aligned(q_packed, 4) || !aligned(global_scale, 4)) return MXQ_EALIGN;
     if (!fits(rows, cols)) return MXQ_ESIZE;
+    return MXQ_OK;
+}
+
+mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
+                          uint8_t *s_e4m3, float *global_scale, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    mxq_status st = check_nvfp4(x, rows, cols, q_packed, s_e4m3, global_scale);
+    if (st != MXQ_OK || rows == 0 || cols == 0) return st;
+    if (!workspace) return MXQ_EINVAL;
+    if (workspace_bytes < nvfp4_workspace_size()) return MXQ_ESIZE;
+    if (!aligned(workspace, 4)) return MXQ_EALIGN;
     return from_hip(mxq::launch_nvfp4_quant(x, rows, cols, q_packed, s_e4m3, global_scale,
-                                            static_cast<uint32_t *>(workspace), as_stream(stream)));
+                                            static_cast<uint32_t *>(workspace),
+                                            (int64_t)(workspace_bytes / sizeof(uint32_t)),
+                                            as_stream(stream)));
+}
+
+mxq_status nvfp4_quantize_noalloc(const uint16_t *x, int64_t rows, int64_t cols,
+                                  uint8_t *q_packed, uint8_t *s_e4m3, float *global_scale,
+                                  void *stream)
+{
+    mxq_status st = check_nvfp4(x, rows, cols, q_packed, s_e4m3, global_scale);
+    if (st != MXQ_OK || rows == 0 || cols == 0) return st;
+    const hipError_t err = mxq::launch_nvfp4_quant_noalloc(x, rows, cols, q_packed, s_e4m3,
+                                                           global_scale, as_stream(stream));
+    return err == hipErrorInvalidValue ? MXQ_ESIZE : from_hip(err);
 }
 
 size_t nvfp4_grouped_workspace_size(const nvfp4_group_desc *descs, int32_t n)

@@ -40,7 +40,10 @@
  *   - Outputs are fully overwritten; no byte outside them is written.
  *   - rows == 0 is accepted and launches nothing (all pointers may then be
  *     NULL).  Sizes must satisfy the per-call shape rules and fit int64.
- *   - The library keeps no state: calls from several host threads are safe.
+ *   - The library keeps no state, except the one device array per GPU that
+ *     nvfp4_quantize_noalloc uses in place of a workspace: calls from several
+ *     host threads are safe, apart from overlapping nvfp4_quantize_noalloc
+ *     calls on one GPU.
  *   - Non-finite inputs: an MX group, block-FP8 tile or NVFP4 tensor that
  *     holds NaN or Inf is quantized as all-NaN (E8M0 byte 0xFF / fp32 NaN
  *     scale / E4M3 0x7F with each element's sign; NVFP4, whose E2M1 has no
@@ -332,6 +335,23 @@ size_t nvfp4_workspace_size(void);
 mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q_packed,
                           uint8_t *s_e4m3, float *global_scale, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * nvfp4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and errors minus the workspace.  The amax
+ * partials go to a fixed array of the library instead: 1024 words (4 KiB)
+ * per GPU, held until the process ends, its device address resolved once per
+ * device on the first call there.  Every size nvfp4_quantize accepts fits
+ * (the amax pass writes at most 1024 partials whatever the size; a launch
+ * that would need more returns MXQ_ESIZE).  The call allocates nothing and
+ * copies nothing.  All calls on one GPU share the array: calls that overlap
+ * on one GPU (several streams or host threads at once) race, so serialize
+ * them.  Nothing in the array needs clearing between calls.
+ */
+mxq_status nvfp4_quantize_noalloc(const uint16_t *x, int64_t rows, int64_t cols,
+                                  uint8_t *q_packed, uint8_t *s_e4m3, float *global_scale,
+                                  void *stream);
 
 /*
  * Grouped NVFP4 with global scales shared within scale groups (xorl PR #30,

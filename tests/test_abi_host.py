@@ -254,6 +254,23 @@ def test_blockfp8_1x128_errors(lib):
     assert fq(P16, 4, 12, P16, NULL) == mxq.MXQ_ESHAPE
 
 
+def test_nvfp4_noalloc_errors(lib):
+    """The allocation-free NVFP4 entry point validates like nvfp4_quantize
+    (minus the workspace) before touching the GPU."""
+    f = lib.nvfp4_quantize_noalloc
+    assert f(P16, -1, 32, P16, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 24, P16, P16, P16, NULL) == mxq.MXQ_ESHAPE          # cols % 16
+    assert f(NULL, 4, 32, P16, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, NULL, P16, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, P16, NULL, P16, NULL) == mxq.MXQ_EINVAL
+    assert f(P16, 4, 32, P16, P16, NULL, NULL) == mxq.MXQ_EINVAL          # no global scale
+    assert f(P8, 4, 32, P16, P16, P16, NULL) == mxq.MXQ_EALIGN            # x 16-aligned
+    assert f(P16, 4, 32, P2, P16, P16, NULL) == mxq.MXQ_EALIGN            # q 4-aligned
+    assert f(P16, 4, 32, P16, P16, P2, NULL) == mxq.MXQ_EALIGN            # g 4-aligned
+    assert f(P16, 1 << 62, 1 << 4, P16, P16, P16, NULL) == mxq.MXQ_ESIZE  # rows * cols overflows
+    assert f(NULL, 0, 32, NULL, NULL, NULL, NULL) == mxq.MXQ_OK
+
+
 def test_nvfp4_grouped_errors(lib):
     f = lib.nvfp4_quantize_grouped
     descs = (mxq.NvGroupDesc * 2)()
