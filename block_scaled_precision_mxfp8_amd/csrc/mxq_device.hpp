@@ -211,9 +211,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 (finite or Inf) -> packed bf16 (a in the low half), RNE.  One
-// v_cvt_pk_bf16_f32: on MI355X it gave exactly bf16_rne's result for every
-// non-NaN fp32 pattern (all 2^32 checked: subnormals kept, overflow to Inf);
-// NaN inputs give a NaN of the same sign, but callers route NaN elsewhere.
+// v_cvt_pk_bf16_f32.  tests/test_gpu_converters.py runs it (and bf16_rne
+// above) on every non-NaN fp32 pattern of both signs against the oracle's
+// bf16 rounding: identical, subnormals kept, overflow to Inf.  NaN inputs
+// give a NaN of the same sign, but callers route NaN elsewhere.
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b)
 {
     const f32x2 v = {a, b};
@@ -256,6 +257,7 @@ __device__ __forceinline__ uint2 mx_dequant4(uint32_t c, int e_dq, bool nan_scal
 // Normal range (t >= 2^-6): round the fp32 pattern at bit 20 and rebias the
 // exponent by 120.  Subnormal range: adding 2^14 rounds t to a multiple of
 // 2^-9 (fp32's step at 2^14), and the low bits of the sum count those steps.
+// Swept with cvt_fp8x2_f32 in tests/test_gpu_converters.py.
 __device__ __forceinline__ uint32_t e4m3_mag_from_f32(float t)
 {
     uint32_t a = __float_as_uint(t);
@@ -267,7 +269,8 @@ __device__ __forceinline__ uint32_t e4m3_mag_from_f32(float t)
 
 // |t| (nonneg fp32, not NaN) -> E2M1 magnitude code 0..7, RNE, saturating.
 // Normal range (t >= 1): round at fp32 bit 22 and rebias by 126.  Below 1:
-// adding 2^22 rounds to a multiple of 0.5.
+// adding 2^22 rounds to a multiple of 0.5.  Swept with cvt_fp4x2_f32 in
+// tests/test_gpu_converters.py.
 __device__ __forceinline__ uint32_t e2m1_mag_from_f32(float t)
 {
     uint32_t a = __float_as_uint(t);
@@ -287,13 +290,14 @@ __device__ __forceinline__ float e2m1_mag_value(uint32_t mag)
 // ---------------------------------------------------------------------------
 // Hardware-assisted MX encode / decode (gfx950 scaled converts).
 //
-// v_cvt_scalef32_pk_fp8_bf16 converts two bf16 to E4M3 as RNE(x / scale).
-// Run over every bf16 pattern and 17 power-of-two scales from 2^-127 to
-// 2^127 on MI355X, it returned exactly the reference encoding for every
-// |x / scale| <= 464, including E4M3 subnormals, signed zeros and bf16
-// subnormal inputs; above that it returns the NaN code instead of
-// saturating.  Clamping each magnitude to 448 * scale first (exact: a bf16
-// value) therefore makes it the saturating RNE encoder of the method.
+// v_cvt_scalef32_pk_fp8_bf16 converts two bf16 to E4M3 as RNE(x / scale),
+// exactly for every |x / scale| <= 464 (E4M3 subnormals, signed zeros and
+// bf16 subnormal inputs included); above that it returns the NaN code
+// instead of saturating.  Clamping each magnitude to 448 * scale first
+// (exact: a bf16 value) therefore makes it the saturating RNE encoder of the
+// method.  tests/test_gpu_parity.py runs every (bf16 value, reachable scale
+// byte) pair through the row kernels (test_rowwise_every_value_every_scale)
+// and the column kernels (test_colwise_edge_values) against the oracle.
 // ---------------------------------------------------------------------------
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
@@ -374,11 +378,13 @@ __device__ __forceinline__ uint32_t e4m3_colpair_hw(uint32_t a, uint32_t b, floa
     return cvt_fp8x2<true>(cvt_fp8x2<false>(0u, lo, s_lo), hi, s_hi);
 }
 
-// MX dequantization with v_cvt_scalef32_pk_bf16_fp8 (E4M3 * scale -> bf16).
-// Over all 256 codes x every E8M0 scale 2^-127..2^127 on MI355X it matched
-// the reference bit for bit -- bf16 subnormal results and overflow to Inf
-// included -- except the NaN codes, which it turns into 0xFFC0 whatever
-// their sign; callers route groups that can hold NaN to mx_dequant4.
+// MX dequantization with v_cvt_scalef32_pk_bf16_fp8 (E4M3 * scale -> bf16):
+// exact for every code and every E8M0 scale 2^-127..2^127 -- bf16 subnormal
+// results and overflow to Inf included -- except the NaN codes, which it
+// turns into 0xFFC0 whatever their sign; callers route groups that can hold
+// NaN to mx_dequant4.  tests/test_gpu_parity.py
+// (test_dequant_hw_path_all_finite_pairs) runs every finite code with every
+// scale byte through this path against the oracle.
 __device__ __forceinline__ uint2 mx_dequant4_hw(uint32_t c, float scale)
 {
     const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false);
@@ -392,14 +398,16 @@ __device__ __forceinline__ uint2 mx_dequant4_hw(uint32_t c, float scale)
 
 // x / d for d > 0 from y = RN(1/d) with two FMAs (Markstein's correction
 // step), the sign taken from x (the correction alone turns -0 into +0).
-// Checked on the host against IEEE division: for every bf16 significand of x,
-// every fp32 significand of d and five quotient binades the results are
-// identical (5.4e9 cases); over every bf16 x (zeros, subnormals, both signs)
-// with |x| <= 512 d, d at 2^-60, 2^-30, 1, 2^30 and 2^59 times every 61st
-// significand (2.4e10 cases) they are identical except for quotients below
-// 2^-30, where both stay below 2^-30 with the same sign -- far under every
-// rounding threshold of E4M3 and E2M1.  Callers therefore use it only for d
-// in [2^-60, 2^60] and quotients of magnitude <= 512.
+// tests/markstein_check.c replays these fp32 operations on the host against
+// IEEE division over the domain the callers use -- d in [2^-60, 2^60],
+// quotients of magnitude <= 512 -- on every bf16 significand of x against
+// every fp32 significand of d in one divisor binade and every 61st in seven
+// others, at ten quotient binades, and on every bf16 pattern of x (zeros,
+// subnormals, both signs) against divisors at 2^-60, 2^-30, 1, 2^30, 2^59
+// times every 61st significand and 2^60 (4.7e10 cases with --runslow, a
+// sample by default): identical except quotients below 2^-30, where both stay
+// below 2^-30 with the same sign -- far under every rounding threshold of
+// E4M3 and E2M1.  Outside that domain callers divide.
 __device__ __forceinline__ float div_markstein(float x, float d, float y)
 {
     const float q0 = x * y;
@@ -413,9 +421,10 @@ __device__ __forceinline__ bool markstein_ok(float d)
 }
 
 // Two fp32 -> E4M3 codes (RNE, saturating) into half kHi of old.
-// v_cvt_pk_fp8_f32 matched the reference for every |t| <= 448 tried on
-// MI355X (all bf16 patterns and 65,536 random full-precision fp32 values);
-// above 448 it gives the NaN code, hence the clamp.
+// v_cvt_pk_fp8_f32 gives the NaN code above 448, hence the clamp; with it,
+// tests/test_gpu_converters.py finds both halves equal to the oracle's E4M3
+// encoding for every fp32 in [-512, 512] and every 4099th pattern up to
+// +-Inf (the quotients x / S stay within 448 (1 + 2^-23)).
 template <bool kHi>
 __device__ __forceinline__ uint32_t cvt_fp8x2_f32(uint32_t old, float a, float b)
 {
@@ -425,8 +434,10 @@ __device__ __forceinline__ uint32_t cvt_fp8x2_f32(uint32_t old, float a, float b
 }
 
 // Two fp32 -> E2M1 nibbles (RNE, saturating at +-6; lo nibble <- a) into byte
-// kByte of old.  v_cvt_scalef32_pk_fp4_f32 with scale 1 matched the reference
-// on all bf16 patterns and 65,536 random fp32 values, saturation included.
+// kByte of old.  tests/test_gpu_converters.py finds v_cvt_scalef32_pk_fp4_f32
+// (scale 1) equal to the oracle's E2M1 encoding in all four byte slots for
+// every fp32 in [-16, 16] and every 4099th pattern up to +-Inf, saturation
+// included (the quotients x / eff stay below 9).
 template <int kByte>
 __device__ __forceinline__ uint32_t cvt_fp4x2_f32(uint32_t old, float a, float b)
 {
@@ -518,8 +529,9 @@ __device__ __forceinline__ uint32_t mx4_scale_byte(uint32_t amag)
 // 8 bf16 (v.x holds elements 0, 1; v.w elements 6, 7) -> 8 E2M1 nibbles of
 // x / sf.  v_cvt_scalef32_pk_fp4_bf16 computes exactly the round-to-nearest-
 // even, +-6-saturating, sign-keeping nibble of x / sf for every bf16 x and
-// power-of-two sf from 2^-127 to 2^127 (probed on MI355X over all 65,536
-// patterns at each of 17 scales including both ends).
+// power-of-two sf from 2^-127 to 2^127; tests/test_gpu_mxfp4.py runs every
+// (bf16 value, reachable scale byte) pair through the MXFP4 kernel against
+// the oracle.
 __device__ __forceinline__ uint32_t e2m1x8_hw(uint4 v, float sf)
 {
     uint32_t o = 0u;
