@@ -212,9 +212,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 (finite or Inf) -> packed bf16 (a in the low half), RNE.  One
 // v_cvt_pk_bf16_f32.  tests/test_gpu_converters.py runs it (and bf16_rne
-// above) on every non-NaN fp32 pattern of both signs against the oracle's
-// bf16 rounding: identical, subnormals kept, overflow to Inf.  NaN inputs
-// give a NaN of the same sign, but callers route NaN elsewhere.
+// above) on every non-NaN fp32 pattern of both signs against the CPU
+// reference's bf16 rounding: identical, subnormals kept, overflow to Inf.
+// NaN inputs give a NaN of the same sign, but callers route NaN elsewhere.
 __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b)
 {
     const f32x2 v = {a, b};
@@ -297,7 +297,7 @@ __device__ __forceinline__ float e2m1_mag_value(uint32_t mag)
 // (exact: a bf16 value) therefore makes it the saturating RNE encoder of the
 // method.  tests/test_gpu_parity.py runs every (bf16 value, reachable scale
 // byte) pair through the row kernels (test_rowwise_every_value_every_scale)
-// and the column kernels (test_colwise_edge_values) against the oracle.
+// and the column kernels (test_colwise_edge_values) against the CPU reference.
 // ---------------------------------------------------------------------------
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
@@ -384,7 +384,7 @@ __device__ __forceinline__ uint32_t e4m3_colpair_hw(uint32_t a, uint32_t b, floa
 // turns into 0xFFC0 whatever their sign; callers route groups that can hold
 // NaN to mx_dequant4.  tests/test_gpu_parity.py
 // (test_dequant_hw_path_all_finite_pairs) runs every finite code with every
-// scale byte through this path against the oracle.
+// scale byte through this path against the CPU reference.
 __device__ __forceinline__ uint2 mx_dequant4_hw(uint32_t c, float scale)
 {
     const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, scale, false);
@@ -422,9 +422,9 @@ __device__ __forceinline__ bool markstein_ok(float d)
 
 // Two fp32 -> E4M3 codes (RNE, saturating) into half kHi of old.
 // v_cvt_pk_fp8_f32 gives the NaN code above 448, hence the clamp; with it,
-// tests/test_gpu_converters.py finds both halves equal to the oracle's E4M3
-// encoding for every fp32 in [-512, 512] and every 4099th pattern up to
-// +-Inf (the quotients x / S stay within 448 (1 + 2^-23)).
+// tests/test_gpu_converters.py finds both halves equal to the CPU
+// reference's E4M3 encoding for every fp32 in [-512, 512] and every 4099th
+// pattern up to +-Inf (the quotients x / S stay within 448 (1 + 2^-23)).
 template <bool kHi>
 __device__ __forceinline__ uint32_t cvt_fp8x2_f32(uint32_t old, float a, float b)
 {
@@ -435,9 +435,9 @@ __device__ __forceinline__ uint32_t cvt_fp8x2_f32(uint32_t old, float a, float b
 
 // Two fp32 -> E2M1 nibbles (RNE, saturating at +-6; lo nibble <- a) into byte
 // kByte of old.  tests/test_gpu_converters.py finds v_cvt_scalef32_pk_fp4_f32
-// (scale 1) equal to the oracle's E2M1 encoding in all four byte slots for
-// every fp32 in [-16, 16] and every 4099th pattern up to +-Inf, saturation
-// included (the quotients x / eff stay below 9).
+// (scale 1) equal to the CPU reference's E2M1 encoding in all four byte
+// slots for every fp32 in [-16, 16] and every 4099th pattern up to +-Inf,
+// saturation included (the quotients x / eff stay below 9).
 template <int kByte>
 __device__ __forceinline__ uint32_t cvt_fp4x2_f32(uint32_t old, float a, float b)
 {
@@ -531,7 +531,7 @@ __device__ __forceinline__ uint32_t mx4_scale_byte(uint32_t amag)
 // even, +-6-saturating, sign-keeping nibble of x / sf for every bf16 x and
 // power-of-two sf from 2^-127 to 2^127; tests/test_gpu_mxfp4.py runs every
 // (bf16 value, reachable scale byte) pair through the MXFP4 kernel against
-// the oracle.
+// the CPU reference.
 __device__ __forceinline__ uint32_t e2m1x8_hw(uint4 v, float sf)
 {
     uint32_t o = 0u;
