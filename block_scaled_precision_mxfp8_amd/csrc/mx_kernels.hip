@@ -25,12 +25,18 @@ namespace mxq {
 
 constexpr int kSeg = 512;          // columns per wave segment
 // Rows per row-wise workgroup tile; each of the 4 waves keeps all its rows in
-// flight.  With cold inputs on [16384, 7168], against 32-row tiles: 16 rows
-// made row-wise 1-2%, fake-quant 4% and the grouped MoE launch 6% faster;
-// 8 rows gained another 2% (row-wise) and 1.6% (fake-quant) for single
-// tensors but lost 4.5% on the grouped launch.
-constexpr int kRowsRow = 8;       // single tensor (4 waves x 2 rows)
+// flight.  With cold inputs on [16384, 7168], against 32-row tiles, 16 rows
+// made fake-quant 4% and the grouped MoE launch 6% faster, and 8 rows gained
+// another 1.6% for single-tensor fake-quant but lost 4.5% on the grouped
+// launch.  For single-tensor quantize-only launches, 16 rows measured 1.5-1.8%
+// faster than 8 on [16384, 7168] and 2-3.5% on [4097, 7168] (interleaved A/B
+// timing, two boxes); launches that write the fake-quant keep 8.
+constexpr int kRowsRowQ = 16;     // single tensor, codes and scales only (4 waves x 4 rows)
+constexpr int kRowsRowFQ = 8;     // single tensor with fake-quant output (4 waves x 2 rows)
 constexpr int kRowsGrouped = 16;  // grouped launch (4 waves x 4 rows)
+
+// Tile rows of a single-tensor row-wise launch.
+constexpr int rows_row_tile(bool q, bool fq) { return (q && !fq) ? kRowsRowQ : kRowsRowFQ; }
 // Rows per dequantize tile (4 waves x 2 rows).  Against 32-row tiles, 16 rows
 // were 3% (row groups) and 7% (column groups) faster, and 8 rows another 1%
 // and 1.5%.
@@ -126,14 +132,15 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
 {
     // quantize-only: a row block's segments run on one XCD, so each row's
     // scale line fills inside one L2 (as the MXFP4 quantizer does)
+    constexpr int kRowsT = rows_row_tile(kQ, kFQ);
     int64_t seg, rb;
     if (kQ && !kFQ) {
-        if (!xcd_row_tile(nseg, (rows + kRowsRow - 1) / kRowsRow, seg, rb)) return;
+        if (!xcd_row_tile(nseg, (rows + kRowsT - 1) / kRowsT, seg, rb)) return;
     } else {
         seg = blockIdx.x % nseg;
         rb = blockIdx.x / nseg;
     }
-    mx_row_tile<kQ, kFQ, kRowsRow>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, seg, rb);
+    mx_row_tile<kQ, kFQ, kRowsT>(x, rows, cols, ldx, q, ldq, scale, lds, fq, ldf, seg, rb);
 }
 
 // ---------------------------------------------------------------------------
@@ -729,9 +736,10 @@ hipError_t launch_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int6
                              int64_t ldf, hipStream_t stream)
 {
     const int64_t nseg = (cols + kSeg - 1) / kSeg;
-    const int64_t nrb = (rows + kRowsRow - 1) / kRowsRow;
+    const int kRowsT = rows_row_tile(q != nullptr, fq != nullptr);
+    const int64_t nrb = (rows + kRowsT - 1) / kRowsT;
     if (nseg <= 0 || nrb <= 0) return hipSuccess;
-    const int64_t tiles = (q && !fq) ? xcd_row_grid(nseg, nrb) : nseg * nrb;
+    const int64_t tiles = (q && !fq) ? xcd_row_grid(nseg, nrb) : nseg * nrb;  // the kernel's order
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)tiles), block(256);
     if (q && fq)
