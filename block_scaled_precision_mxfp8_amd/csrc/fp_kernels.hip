@@ -356,10 +356,13 @@ __global__ __launch_bounds__(256) void bfp8_to_mx_kernel(const uint8_t *__restri
 // NVFP4.  Pass 1: each workgroup writes the max magnitude (bf16 bits) of its
 // share of x to a partials array; one workgroup reduces the partials (an
 // unsigned max: order-independent, deterministic) to g, written to the
-// caller's global-scale word; pass 2 reads g and quantizes.  (Reducing the
-// partials in every encoding workgroup instead cost each of them a 4 KiB read
-// and a barrier.)  In pass 2 a lane pair owns one 16-element block: 16 bytes
-// of x, 4 bytes of packed codes and (both lanes) its scale byte each.
+// caller's global-scale word; pass 2 reads g and quantizes.  Measured on
+// MI355X ([8192, 8192], cold): reducing the partials in the encoding pass
+// instead -- in one wave behind a barrier, or in every wave, 256 or 512 of
+// them, or once per workgroup of a persistent encoding grid -- made that pass
+// 2 to 13 us slower, more than the reducing launch costs (about 5 us).  In
+// pass 2 a lane pair owns one 16-element block: 16 bytes of x, 4 bytes of
+// packed codes and (both lanes) its scale byte each.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t *__restrict__ x,
@@ -506,19 +509,20 @@ __device__ __forceinline__ void nvfp4_load_rows(const uint16_t *__restrict__ x, 
     }
 }
 
-// One workgroup: the global amax from the partials, g = fl32(A / 2688) (NaN
-// when x holds NaN/Inf), written once for the encoding pass to read.
-__global__ __launch_bounds__(256) void nvfp4_finalize_kernel(const uint32_t *__restrict__ partial,
-                                                             int npartial, float *__restrict__ g_out)
+// One workgroup: the global amax from the partials (one per thread, so every
+// load is in flight at once), g = fl32(A / 2688) (NaN when x holds NaN/Inf),
+// written once for the encoding pass to read.
+__global__ __launch_bounds__(kNvAmaxBlocks) void nvfp4_finalize_kernel(
+    const uint32_t *__restrict__ partial, int npartial, float *__restrict__ g_out)
 {
-    __shared__ uint32_t red[4];
-    uint32_t am = 0;
-    for (int k = threadIdx.x; k < npartial; k += 256) am = max(am, partial[k]);
+    __shared__ uint32_t red[kNvAmaxBlocks / kWave];
+    uint32_t am = (int)threadIdx.x < npartial ? partial[threadIdx.x] : 0u;
     am = wave_max(am);
     if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = am;
     __syncthreads();
     if (threadIdx.x == 0) {
-        am = max(max(red[0], red[1]), max(red[2], red[3]));
+#pragma unroll
+        for (int w = 1; w < kNvAmaxBlocks / kWave; ++w) am = max(am, red[w]);
         const bool nonfinite = am >= 0x7F80u;
         *g_out = nonfinite ? __builtin_nanf("") : __uint_as_float(am << 16) / 2688.0f;  // 448 * 6
     }
@@ -795,7 +799,8 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(nvfp4_finalize_kernel, dim3(1), dim3(256), 0, stream, ws, ablocks, g);
+    hipLaunchKernelGGL(nvfp4_finalize_kernel, dim3(1), dim3(kNvAmaxBlocks), 0, stream, ws, ablocks,
+                       g);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,
@@ -805,7 +810,7 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
 
 // ---------------------------------------------------------------------------
 // NVFP4 for callers that cannot allocate: the amax partials go to `scratch`,
-// a fixed array of this library (kNvAmaxBlocks words, 4 KiB) that each GPU
+// a fixed array of this library (kNvAmaxBlocks words, 2 KiB) that each GPU
 // holds until the process ends, instead of a caller workspace.  In host code
 // `scratch` names a host-side stand-in, not device memory: its address on a
 // device comes from hipGetSymbolAddress, resolved once per device with that

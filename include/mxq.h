@@ -340,10 +340,10 @@ mxq_status nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t
  * nvfp4_quantize for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments, results and errors minus the workspace.  The amax
- * partials go to a fixed array of the library instead: 1024 words (4 KiB)
+ * partials go to a fixed array of the library instead: 512 words (2 KiB)
  * per GPU, held until the process ends, its device address resolved once per
  * device on the first call there.  Every size nvfp4_quantize accepts fits
- * (the amax pass writes at most 1024 partials whatever the size; a launch
+ * (the amax pass writes at most 512 partials whatever the size; a launch
  * that would need more returns MXQ_ESIZE).  The call allocates nothing and
  * copies nothing.  All calls on one GPU share the array: calls that overlap
  * on one GPU (several streams or host threads at once) race, so serialize
