@@ -23,14 +23,16 @@ Besides the timed steps it reports, in the same line:
                 from the committed rocprofv3 counter summary when it still
                 matches the kernel source
   ceilings      per read:write mix (read, write, copy, row-wise quantize,
-                one-pass), the best rate of several trivial-arithmetic
+                one-pass, dequantize, FP4 encode, FP4 dequantize), the best
+                rate of several trivial-arithmetic
                 streaming patterns (bench_streams.hip) over the same cold
                 batches; ceiling_runs lists every pattern's rate
   cpu_baseline  the CPU oracle (single-threaded C) timed on a bounded sample
                 of the same workload, and the same sharded over host threads
   breakdown     every other quantizer workload (row-wise weight, grouped MoE
                 experts, block-FP8, NVFP4, dequantizers), each timed on its own;
-                the MXFP8 quantizers also as a fraction of their mix's ceiling
+                the quantizers and dequantizers also as a fraction of their
+                mix's ceiling (measured on the [16384, 7168] batches)
 """
 from __future__ import annotations
 
@@ -100,6 +102,7 @@ def load_streams():
     L.bench_stream_tiled.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, vp, vp, vp, vp]
     L.bench_stream_flat.restype = ctypes.c_int
     L.bench_stream_flat.argtypes = [ctypes.c_int, vp, i64, vp, vp, vp, vp, ctypes.c_int, vp]
+    L.bench_streams_kinds.restype = ctypes.c_int
     return L
 
 
@@ -133,60 +136,80 @@ def read_traffic(workload: str):
     return None
 
 
-MIX_BYTES = {  # bytes moved per element by each streaming-ceiling mix (tiled / flat)
+# Streaming-ceiling mixes in bench_streams.hip's kind order, and the bytes each
+# moves per element (tiled patterns, which carry the scale stream; flat ones).
+MIXES = ["read", "write", "copy", "row", "onepass", "dequant", "fp4", "fp4dq"]
+MIX_BYTES = {
     "read": (2.0, 2.0), "write": (2.0, 2.0), "copy": (4.0, 4.0),
-    "row": (3.0 + 1 / 32, 3.0), "onepass": (6.0 + 1 / 32, 6.0)}
-MIXES = ["read", "write", "copy", "row", "onepass"]   # tiled variant order
-FLAT_MODES = ["read", "copy", "row", "onepass", "write"]
+    "row": (3.0 + 1 / 32, 3.0), "onepass": (6.0 + 1 / 32, 6.0),
+    "dequant": (3.0 + 1 / 32, 3.0), "fp4": (2.5 + 1 / 32, 2.5), "fp4dq": (2.5 + 1 / 32, 2.5)}
+MIX_DESC = {
+    "read": "2 B read per element", "write": "2 B written", "copy": "2 B read : 2 written",
+    "row": "2 B read : 1 + 1/32 written", "onepass": "2 B read : 4 + 1/16 written",
+    "dequant": "1 + 1/32 B read : 2 written", "fp4": "2 B read : 1/2 + 1/32 written",
+    "fp4dq": "1/2 + 1/32 B read : 2 written"}
 
 
 def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
     """Best GB/s per mix over the tiled (R = 1, 2, 4, 8 rows per wave) and flat
-    (U = 2, 4, 8 loads in flight; 1024, 2048, 4096 workgroups) patterns, each
-    timed like the quantizers: back-to-back launches cycling over the cold
-    batches after an untimed warm-up."""
+    (U = 2, 4, 8 vectors in flight; 1024, 2048, 4096 workgroups) patterns,
+    each timed like the quantizers: back-to-back launches cycling over cold
+    inputs after an untimed warm-up.  The mixes that read x cycle over the
+    batches, as the bench step does.  The two that read codes (1 B or 1/2 B per
+    element) would find 4 batches' codes in the 256 MB Infinity Cache, so they
+    cycle over every code region the batches hold (8 for 1-byte codes, 16 for
+    half-byte ones): 0.85-0.93 GB of other codes pass between two reads of one."""
     import torch
+    assert L.bench_streams_kinds() == len(MIXES)
     e = rows * cols
     sink = torch.empty((16,), dtype=torch.int32, device=batches[0]["x"].device)
 
-    def P(t):
-        return ctypes.c_void_p(t.data_ptr())
+    def A(t, off=0):
+        return ctypes.c_void_p(t.data_ptr() + off)
 
-    def timed(launch):
-        for i in range(max(16, len(batches))):
-            launch(batches[i % len(batches)])
+    # per mix: the argument sets (x, codes, o8b, o16, row scales) it cycles over
+    plain = [(A(d["x"]), A(d["qc"]), A(d["qr"]), A(d["fq"]), A(d["sr"])) for d in batches]
+    codes1 = [(A(d["x"]), A(d[k]), A(d["qr"]), A(d["fq"]), A(d["sr"]))
+              for k in ("qc", "qr") for d in batches]
+    codes_half = [(A(d["x"]), A(d[k], h * (e // 2)), A(d["qr"]), A(d["fq"]), A(d["sr"]))
+                  for k in ("qc", "qr") for h in (0, 1) for d in batches]
+    sources = {m: plain for m in MIXES}
+    sources["dequant"], sources["fp4dq"] = codes1, codes_half
+
+    def timed(launch, srcs):
+        for i in range(max(16, len(srcs))):
+            launch(srcs[i % len(srcs)])
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for i in range(iters):
-            launch(batches[i % len(batches)])
+            launch(srcs[i % len(srcs)])
         b.record(stream)
         b.synchronize()
         return a.elapsed_time(b) / iters * 1e-3
 
     runs = {}
-    for v in range(20):
+    for v in range(4 * len(MIXES)):
         mix, R = MIXES[v // 4], 1 << (v % 4)
 
-        def go(d, v=v):
-            st = L.bench_stream_tiled(v, P(d["x"]), rows, cols, P(d["qc"]), P(d["qr"]), P(d["fq"]),
-                                      P(d["sr"]), P(sink), sp)
+        def go(a, v=v):
+            st = L.bench_stream_tiled(v, a[0], rows, cols, a[1], a[2], a[3], a[4], A(sink), sp)
             if st != 0:
                 raise RuntimeError(f"bench_stream_tiled({v}) status {st}")
-        runs[f"{mix} tiled R{R}"] = (mix, MIX_BYTES[mix][0] * e / timed(go) / 1e9)
-    for v in range(15):
-        mix, U = FLAT_MODES[v // 3], (2, 4, 8)[v % 3]
+        runs[f"{mix} tiled R{R}"] = (mix, MIX_BYTES[mix][0] * e / timed(go, sources[mix]) / 1e9)
+    for v in range(3 * len(MIXES)):
+        mix, U = MIXES[v // 3], (2, 4, 8)[v % 3]
         for grid in (1024, 2048, 4096):
-            def go(d, v=v, grid=grid):
-                st = L.bench_stream_flat(v, P(d["x"]), e // 8, P(d["qc"]), P(d["qr"]), P(d["fq"]),
-                                         P(sink), grid, sp)
+            def go(a, v=v, grid=grid):
+                st = L.bench_stream_flat(v, a[0], e // 8, a[1], a[2], a[3], A(sink), grid, sp)
                 if st != 0:
                     raise RuntimeError(f"bench_stream_flat({v}) status {st}")
-            runs[f"{mix} flat U{U} grid{grid}"] = (mix, MIX_BYTES[mix][1] * e / timed(go) / 1e9)
+            runs[f"{mix} flat U{U} grid{grid}"] = (
+                mix, MIX_BYTES[mix][1] * e / timed(go, sources[mix]) / 1e9)
     best = {}
     for name, (mix, gbs) in runs.items():
         if mix not in best or gbs > best[mix]["GB/s"]:
-            best[mix] = {"GB/s": round(gbs, 1), "pattern": name}
+            best[mix] = {"GB/s": round(gbs, 1), "pattern": name, "bytes": MIX_DESC[mix]}
     return best, {k: round(g, 1) for k, (_, g) in runs.items()}
 
 
@@ -430,7 +453,7 @@ def main():
             breakdown[f"act_16384 {nm} dequantize"] = rotated(
                 [lambda d=d, ax=ax: check(
                     lib.mxq_dequantize(P(d["q"]), P(d["s"]), rows, cols, ax, P(d["out"]), sp),
-                    "dequantize") for d in dq], e + batches[0][sk].numel() + 2 * e)
+                    "dequantize") for d in dq], e + batches[0][sk].numel() + 2 * e, mix="dequant")
             del dq
         # column-wise in the transposed (backward-pass) layout, with and
         # without the row-wise outputs of the same pass
@@ -438,34 +461,34 @@ def main():
             [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]), rows,
                                                           P(d["st"]), P(d["qr"]), P(d["sr"]),
                                                           P(d["fq"]), sp), "colwise_t")
-             for d in batches], step_bytes)
+             for d in batches], step_bytes, mix="onepass")
         breakdown["act_16384 column-wise transposed only"] = rotated(
             [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]), rows,
                                                           P(d["st"]), None, None, None, sp),
-                               "colwise_t") for d in batches], 2 * e + e + e // 32)
+                               "colwise_t") for d in batches], 2 * e + e + e // 32, mix="row")
         # 1 x 128 block-FP8 (activation recipe) and its simulate-QAT
         b1 = 2 * e + e + 4 * (e // 128)
         breakdown["act_16384 block-FP8 1x128 quantize"] = rotated(
             [lambda d=d: check(lib.blockfp8_quantize_1x128(P(d["x"]), rows, cols, P(d["qr"]),
                                                            P(d["S1"]), None, sp), "bfp8 1x128")
-             for d in batches], b1)
+             for d in batches], b1, mix="row")
         breakdown["act_16384 block-FP8 1x128 simulate-QAT (fake-quant only)"] = rotated(
             [lambda d=d: check(lib.blockfp8_fake_quant_1x128(P(d["x"]), rows, cols, P(d["fq"]),
                                                              sp), "bfp8 1x128 fq")
-             for d in batches], 4 * e)
+             for d in batches], 4 * e, mix="copy")
         # MXFP4 on the same batches: quantize, simulate-QAT, dequantize
         m4 = 2 * e + e // 2 + e // 32
         breakdown["act_16384 MXFP4 quantize"] = rotated(
             [lambda d=d: check(lib.mxfp4_quantize(P(d["x"]), rows, cols, P(d["q4"]), P(d["s4"]),
-                                                  None, sp), "mxfp4") for d in batches], m4)
+                                                  None, sp), "mxfp4") for d in batches], m4, mix="fp4")
         breakdown["act_16384 MXFP4 simulate-QAT (fake-quant only)"] = rotated(
             [lambda d=d: check(lib.mxfp4_fake_quant(P(d["x"]), rows, cols, P(d["fq"]), sp),
-                               "mxfp4 fq") for d in batches], 4 * e)
+                               "mxfp4 fq") for d in batches], 4 * e, mix="copy")
         dq = code_copies("q4", "s4")
         breakdown["act_16384 MXFP4 dequantize"] = rotated(
             [lambda d=d: check(lib.mxfp4_dequantize(P(d["q"]), P(d["s"]), rows, cols, P(d["out"]),
                                                     sp), "mxfp4 dq") for d in dq],
-            e // 2 + e // 32 + 2 * e)
+            e // 2 + e // 32 + 2 * e, mix="fp4dq")
         del batches, dq
         torch.cuda.empty_cache()
 
@@ -480,7 +503,7 @@ def main():
         breakdown["weight_4097 row-wise"] = rotated(
             [lambda t=t: check(lib.mxq_quantize_rowwise(P(t[0]), wr, wc, wc, P(t[1]), wc, P(t[2]),
                                                         wc // 32, None, 0, sp), "rowwise")
-             for t in wsets], wbytes)
+             for t in wsets], wbytes, mix="row")
         del w0, wsets
 
         # mx_small row-wise + dequantize: a latency measurement (the data is
@@ -572,7 +595,7 @@ def main():
         breakdown["square_8192 block-FP8 dequantize"] = rotated(
             [lambda d=d: check(lib.blockfp8_dequantize(P(d["bq"]), P(d["bS"]), n_, n_, 128,
                                                        P(d["bd"]), sp), "bfp8 dq") for d in ysets],
-            bbytes)
+            bbytes, mix="dequant")
         breakdown["square_8192 block-FP8 -> MXFP8 re-quantize (one pass)"] = rotated(
             [lambda d=d: check(lib.blockfp8_to_mxfp8(P(d["bq"]), P(d["bS"]), n_, n_, 128,
                                                      P(d["rq8"]), P(d["rs8"]), sp), "requant")
@@ -584,7 +607,7 @@ def main():
         breakdown["square_8192 NVFP4 dequantize"] = rotated(
             [lambda d=d: check(lib.nvfp4_dequantize(P(d["nq"]), P(d["ns"]), P(d["ng"]), n_, n_,
                                                     P(d["bd"]), sp), "nvfp4 dq") for d in ysets],
-            nbytes)
+            nbytes, mix="fp4dq")
         del ysets
 
     out = {
