@@ -44,13 +44,15 @@ static_assert(kBlk % kRowsDq == 0 && kBlk % kRowsBq == 0,
 // Streaming (non-temporal) hints, chosen by measurement on MI355X with
 // inputs read cold from HBM.  Outputs are written once.  Hinted 16-byte loads
 // of x help block-FP8 (+3%); the dequantizers' 4- and 8-byte code loads do
-// better unhinted (NVFP4: 4.3 -> 5.0 TB/s).  The single-tensor NVFP4 amax
+// better unhinted (NVFP4: 4.3 -> 5.0 TB/s), while the FP8 -> MXFP8 pass's
+// 8-byte code loads measured 2% faster hinted.  The single-tensor NVFP4 amax
 // pass loads unhinted so that x can stay in the Infinity Cache for the
 // encoding pass; the grouped amax pass streams (its tensors together far
 // exceed that cache: 2.87 -> 2.72 ms on 256 MoE gate/up tensors).
 constexpr bool kNTStore = true;
 constexpr bool kNTLoad = true;
 constexpr bool kNTLoadDq = false;
+constexpr bool kNTLoadRequant = true;
 constexpr bool kNTLoadNvAmax = false;
 constexpr bool kNTLoadNvGAmax = true;
 constexpr bool kNTLoadNvQuant = true;
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void bfp8_to_mx_kernel(const uint8_t *__restri
     for (int i = 0; i < kR; ++i) {
         const int64_t r = r0 + 4 * i;
         c[i] = make_uint2(0, 0);
-        if (r < rows) c[i] = ld8<kNTLoadDq>(q + r * cols + col);
+        if (r < rows) c[i] = ld8<kNTLoadRequant>(q + r * cols + col);
         const uint32_t tx = c[i].x & 0x7F7F7F7Fu, ty = c[i].y & 0x7F7F7F7Fu;
         nan_code |= (((tx + 0x01010101u) | (ty + 0x01010101u)) & 0x80808080u) != 0u;
     }
@@ -535,9 +537,11 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t *__rest
                                                           const float *__restrict__ g_in,
                                                           int64_t nseg)
 {
-    const int64_t tile = blockIdx.x;
-    const int64_t seg = tile % nseg;
-    const int64_t rb = tile / nseg;
+    // a row block's segments run on one XCD (2% faster end to end on
+    // [8192, 8192] than the plain order); padding workgroups leave before the
+    // barrier in nvfp4_scale_table, whole
+    int64_t seg, rb;
+    if (!xcd_row_tile(nseg, (rows + kRowsNvQ - 1) / kRowsNvQ, seg, rb)) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegNv + lane * 8;
@@ -794,7 +798,7 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     const int ablocks = (int)(want < kNvAmaxBlocks ? want : kNvAmaxBlocks);
     if (ablocks > ws_words) return hipErrorInvalidValue;  // one partial per amax workgroup
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
-    const int64_t tiles = nseg * ((rows + kRowsNvQ - 1) / kRowsNvQ);
+    const int64_t tiles = xcd_row_grid(nseg, (rows + kRowsNvQ - 1) / kRowsNvQ);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
     hipError_t err = hipGetLastError();
