@@ -23,7 +23,8 @@ Besides the timed steps it reports, in the same line:
                 from the committed rocprofv3 counter summary when it still
                 matches the kernel source
   ceilings      per read:write mix (read, write, copy, row-wise quantize,
-                one-pass, dequantize, FP4 encode, FP4 dequantize), the best
+                one-pass, dequantize, FP4 encode, FP4 dequantize, FP8 block to
+                MXFP8), the best
                 rate of several trivial-arithmetic
                 streaming patterns (bench_streams.hip) over the same cold
                 batches; ceiling_runs lists every pattern's rate
@@ -138,16 +139,17 @@ def read_traffic(workload: str):
 
 # Streaming-ceiling mixes in bench_streams.hip's kind order, and the bytes each
 # moves per element (tiled patterns, which carry the scale stream; flat ones).
-MIXES = ["read", "write", "copy", "row", "onepass", "dequant", "fp4", "fp4dq"]
+MIXES = ["read", "write", "copy", "row", "onepass", "dequant", "fp4", "fp4dq", "requant"]
 MIX_BYTES = {
     "read": (2.0, 2.0), "write": (2.0, 2.0), "copy": (4.0, 4.0),
     "row": (3.0 + 1 / 32, 3.0), "onepass": (6.0 + 1 / 32, 6.0),
-    "dequant": (3.0 + 1 / 32, 3.0), "fp4": (2.5 + 1 / 32, 2.5), "fp4dq": (2.5 + 1 / 32, 2.5)}
+    "dequant": (3.0 + 1 / 32, 3.0), "fp4": (2.5 + 1 / 32, 2.5), "fp4dq": (2.5 + 1 / 32, 2.5),
+    "requant": (2.0 + 1 / 32, 2.0)}
 MIX_DESC = {
     "read": "2 B read per element", "write": "2 B written", "copy": "2 B read : 2 written",
     "row": "2 B read : 1 + 1/32 written", "onepass": "2 B read : 4 + 1/16 written",
     "dequant": "1 + 1/32 B read : 2 written", "fp4": "2 B read : 1/2 + 1/32 written",
-    "fp4dq": "1/2 + 1/32 B read : 2 written"}
+    "fp4dq": "1/2 + 1/32 B read : 2 written", "requant": "1 B read : 1 + 1/32 written"}
 
 
 def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
@@ -155,7 +157,7 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
     (U = 2, 4, 8 vectors in flight; 1024, 2048, 4096 workgroups) patterns,
     each timed like the quantizers: back-to-back launches cycling over cold
     inputs after an untimed warm-up.  The mixes that read x cycle over the
-    batches, as the bench step does.  The two that read codes (1 B or 1/2 B per
+    batches, as the bench step does.  The three that read codes (1 B or 1/2 B per
     element) would find 4 batches' codes in the 256 MB Infinity Cache, so they
     cycle over every code region the batches hold (8 for 1-byte codes, 16 for
     half-byte ones): 0.85-0.93 GB of other codes pass between two reads of one."""
@@ -173,8 +175,11 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
               for k in ("qc", "qr") for d in batches]
     codes_half = [(A(d["x"]), A(d[k], h * (e // 2)), A(d["qr"]), A(d["fq"]), A(d["sr"]))
                   for k in ("qc", "qr") for h in (0, 1) for d in batches]
+    # FP8 block -> MXFP8 writes codes too: to the fake-quant buffer, not the codes it reads
+    codes_rq = [(A(d["x"]), A(d[k]), A(d["fq"]), A(d["fq"]), A(d["sr"]))
+                for k in ("qc", "qr") for d in batches]
     sources = {m: plain for m in MIXES}
-    sources["dequant"], sources["fp4dq"] = codes1, codes_half
+    sources["dequant"], sources["fp4dq"], sources["requant"] = codes1, codes_half, codes_rq
 
     def timed(launch, srcs):
         for i in range(max(16, len(srcs))):
@@ -611,7 +616,7 @@ def main():
             [lambda d=d: check(lib.blockfp8_to_mxfp8(P(d["bq"]), P(d["bS"]), n_, n_, 128,
                                                      P(d["rq8"]), P(d["rs8"]), sp), "requant")
              for d in ysets[:ncopies(ye + 4 * (n_ // 128) ** 2)]],
-            ye + 4 * (n_ // 128) ** 2 + ye + ye // 32)
+            ye + 4 * (n_ // 128) ** 2 + ye + ye // 32, mix="requant")
         breakdown["square_8192 NVFP4 quantize (unique bytes)"] = rotated(
             [lambda d=d: check(lib.nvfp4_quantize(P(d["y"]), n_, n_, P(d["nq"]), P(d["ns"]),
                                                   P(d["ng"]), P(d["nws"]), nwsz, sp), "nvfp4")

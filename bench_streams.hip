@@ -21,6 +21,7 @@
 //   row 2:1+1/32 (3, MXFP8 quantize)   onepass 2:4+1/32 (4, codes of both axes,
 //   row scales, fake-quant)   dequant 1+1/32:2 (5, MXFP8 / FP8 dequantize)
 //   fp4 2:1/2+1/32 (6, MXFP4 / NVFP4 encode)   fp4dq 1/2+1/32:2 (7, FP4 dequantize)
+//   requant 1:1+1/32 (8, FP8 block -> MXFP8: codes in, codes and scales out)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,18 +37,19 @@ using mxq::st4;
 using mxq::st8;
 
 constexpr uint32_t kNever = 0x9E3779B9u;  // the fold of loaded words is compared against this
-constexpr int kKinds = 8;
+constexpr int kKinds = 9;
 
 // What each mix reads and writes per lane and row (tiled) or per element group (flat).
 template <int K>
 struct Mix {
-    static constexpr int rd = (K == 1) ? 0 : (K == 5) ? 8 : (K == 7) ? 4 : 16;  // bytes read
+    static constexpr int rd = (K == 1) ? 0 : (K == 5 || K == 8) ? 8 : (K == 7) ? 4 : 16;  // read
     static constexpr int w8 = (K == 3) ? 1 : (K == 4) ? 2 : 0;                  // 8-byte planes
     static constexpr int w16 = (K == 1 || K == 2 || K == 4 || K == 5 || K == 7) ? 1 : 0;
     static constexpr int w4 = (K == 6) ? 1 : 0;                                 // 4-byte planes
-    static constexpr bool sc_wr = K == 3 || K == 4 || K == 6;                   // scale byte written
+    static constexpr int w8b = (K == 8) ? 1 : 0;  // 8-byte plane in o8b (codes read from o8a)
+    static constexpr bool sc_wr = K == 3 || K == 4 || K == 6 || K == 8;         // scale byte written
     static constexpr bool sc_rd = K == 5 || K == 7;                             // scale byte read
-    static constexpr bool writes = w8 + w16 + w4 > 0 || sc_wr;
+    static constexpr bool writes = w8 + w16 + w4 + w8b > 0 || sc_wr;
 };
 
 // x: the bf16 input for 16-byte reads; codes (o8a) for 8- and 4-byte reads.
@@ -94,6 +96,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__
         if (M::w8 > 1) st8<true>(o8b + r * cols + col, make_uint2(c.y, c.x));
         if (M::w16 > 0) st16<true>(o16 + r * cols + col, v[i]);
         if (M::w4 > 0) st4<true>(o8b + r * (cols >> 1) + (col >> 1), c.x ^ c.y);
+        if (M::w8b > 0) st8<true>(o8b + r * cols + col, c);
         if (M::sc_wr) sc[r * (cols >> 5) + (col >> 5)] = (uint8_t)c.x;
         fold ^= v[i].x ^ v[i].w;
     }
@@ -139,6 +142,7 @@ __global__ __launch_bounds__(256) void flat_kernel(const uint4 *__restrict__ x, 
             if (M::w8 > 0) st8<true>(o8a + i, make_uint2(v[u].x, v[u].z));
             if (M::w8 > 1) st8<true>(o8b + i, make_uint2(v[u].y, v[u].w));
             if (M::w4 > 0) st4<true>(reinterpret_cast<uint32_t *>(o8b) + i, v[u].x ^ v[u].y);
+            if (M::w8b > 0) st8<true>(o8b + i, make_uint2(v[u].x, v[u].z));
             fold ^= v[u].x;
         }
     }
@@ -190,7 +194,8 @@ int bench_stream_tiled(int variant, const void *x, int64_t rows, int64_t cols, v
     case 4: TL(RR, 4); break;                                                                      \
     case 5: TL(RR, 5); break;                                                                      \
     case 6: TL(RR, 6); break;                                                                      \
-    default: TL(RR, 7); break;                                                                     \
+    case 7: TL(RR, 7); break;                                                                      \
+    default: TL(RR, 8); break;                                                                     \
     }
     switch (R) {
     case 1: TL_KIND(1); break;
@@ -229,7 +234,8 @@ int bench_stream_flat(int variant, const void *x, int64_t nvec, void *o8a, void 
     case 4: FL(UU, 4); break;                                                                      \
     case 5: FL(UU, 5); break;                                                                      \
     case 6: FL(UU, 6); break;                                                                      \
-    default: FL(UU, 7); break;                                                                     \
+    case 7: FL(UU, 7); break;                                                                      \
+    default: FL(UU, 8); break;                                                                     \
     }
     switch (ui) {
     case 0: FL_KIND(2); break;
