@@ -153,7 +153,8 @@ MIX_DESC = {
 
 
 def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
-    """Best GB/s per mix over the tiled (R = 1, 2, 4, 8 rows per wave) and flat
+    """Best GB/s per mix over the tiled (R = 1, 2, 4, 8 rows per wave; plain or
+    XCD row-block order) and flat
     (U = 2, 4, 8 vectors in flight; 1024, 2048, 4096 workgroups) patterns,
     each timed like the quantizers: back-to-back launches cycling over cold
     inputs after an untimed warm-up.  The mixes that read x cycle over the
@@ -194,14 +195,15 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
         return a.elapsed_time(b) / iters * 1e-3
 
     runs = {}
-    for v in range(4 * len(MIXES)):
-        mix, R = MIXES[v // 4], 1 << (v % 4)
+    for v in range(8 * len(MIXES)):
+        mix, R = MIXES[(v // 4) % len(MIXES)], 1 << (v % 4)
+        order = " xcd" if v >= 4 * len(MIXES) else ""
 
         def go(a, v=v):
             st = L.bench_stream_tiled(v, a[0], rows, cols, a[1], a[2], a[3], a[4], A(sink), sp)
             if st != 0:
                 raise RuntimeError(f"bench_stream_tiled({v}) status {st}")
-        runs[f"{mix} tiled R{R}"] = (mix, MIX_BYTES[mix][0] * e / timed(go, sources[mix]) / 1e9)
+        runs[f"{mix} tiled R{R}{order}"] = (mix, MIX_BYTES[mix][0] * e / timed(go, sources[mix]) / 1e9)
     for v in range(3 * len(MIXES)):
         mix, U = MIXES[v // 3], (2, 4, 8)[v % 3]
         for grid in (1024, 2048, 4096):

@@ -6,7 +6,8 @@
 // access pattern.  bench.py takes, per mix, the best of several patterns as
 // the ceiling it reports beside the quantizer kernels:
 //   tiled  one workgroup per 512-column x (4 waves x R rows) tile of a
-//          [rows, cols] tensor (the quantizers' own tile shape), per lane and
+//          [rows, cols] tensor (the quantizers' own tile shape), in the
+//          plain segment-fastest order or the quantizers' XCD order, per lane and
 //          row the mix's bytes: 16 bytes of bf16 or 8 (4) bytes of codes read,
 //          8 / 16 / 4 bytes written per plane, and one byte per lane quad and
 //          row (a scale byte per 32 elements) where the mix has scales;
@@ -53,7 +54,7 @@ struct Mix {
 };
 
 // x: the bf16 input for 16-byte reads; codes (o8a) for 8- and 4-byte reads.
-template <int R, int K>
+template <int R, int K, bool X>
 __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t nseg,
                                                     uint8_t *__restrict__ o8a,
@@ -63,7 +64,15 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__
                                                     uint32_t *__restrict__ sink)
 {
     using M = Mix<K>;
-    const int64_t seg = blockIdx.x % nseg, rb = blockIdx.x / nseg;
+    // X: the quantizers' order, a row block's segments on one XCD (so a
+    // row's scale line fills inside one L2); else segment-fastest
+    int64_t seg, rb;
+    if (X) {
+        if (!mxq::xcd_row_tile(nseg, (rows + 4 * R - 1) / (4 * R), seg, rb)) return;
+    } else {
+        seg = blockIdx.x % nseg;
+        rb = blockIdx.x / nseg;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t col = seg * 512 + lane * 8;
@@ -161,7 +170,8 @@ const char *bench_streams_build_id(void) { return STREAMS_BUILD_ID; }
 
 int bench_streams_kinds(void) { return kKinds; }
 
-// Tiled variants: variant = R index (0: R=1, 1: R=2, 2: R=4, 3: R=8) + 4 * kind.
+// Tiled variants: variant = R index (0: R=1, 1: R=2, 2: R=4, 3: R=8) + 4 * kind
+// + 4 * kinds * order (0: segment-fastest, 1: a row block's segments on one XCD).
 // x [rows, cols] bf16 with cols % 512 == 0; o8a, o8b [rows, cols] bytes (the
 // codes the 8- and 4-byte reading kinds read are o8a); o16 [rows, cols] bf16;
 // sc [rows, cols/32] bytes; sink one word.  Returns 0, 1 for a bad argument
@@ -169,13 +179,14 @@ int bench_streams_kinds(void) { return kKinds; }
 int bench_stream_tiled(int variant, const void *x, int64_t rows, int64_t cols, void *o8a,
                        void *o8b, void *o16, void *sc, void *sink, void *stream)
 {
-    if (variant < 0 || variant >= 4 * kKinds || rows <= 0 || cols <= 0 || cols % 512 != 0)
+    if (variant < 0 || variant >= 8 * kKinds || rows <= 0 || cols <= 0 || cols % 512 != 0)
         return 1;
     if (!x || !o8a || !o8b || !o16 || !sc || !sink) return 1;
     const int64_t nseg = cols / 512;
-    const int ri = variant % 4, kind = variant / 4;
+    const int ri = variant % 4, kind = (variant / 4) % kKinds, xcd = variant / (4 * kKinds);
     const int R = 1 << ri;
-    const int64_t tiles = nseg * ((rows + 4 * R - 1) / (4 * R));
+    const int64_t nrb = (rows + 4 * R - 1) / (4 * R);
+    const int64_t tiles = xcd ? mxq::xcd_row_grid(nseg, nrb) : nseg * nrb;
     if (tiles > 0x7FFFFFFF) return 1;
     const hipStream_t s = (hipStream_t)stream;
     const uint16_t *xp = (const uint16_t *)x;
@@ -183,8 +194,14 @@ int bench_stream_tiled(int variant, const void *x, int64_t rows, int64_t cols, v
     uint16_t *f = (uint16_t *)o16;
     uint32_t *k = (uint32_t *)sink;
 #define TL(RR, KK)                                                                                 \
-    hipLaunchKernelGGL((tiled_kernel<RR, KK>), dim3((unsigned)tiles), dim3(256), 0, s, xp, rows,  \
-                       cols, nseg, a, b, f, c, k)
+    do {                                                                                           \
+        if (xcd)                                                                                   \
+            hipLaunchKernelGGL((tiled_kernel<RR, KK, true>), dim3((unsigned)tiles), dim3(256), 0, \
+                               s, xp, rows, cols, nseg, a, b, f, c, k);                            \
+        else                                                                                       \
+            hipLaunchKernelGGL((tiled_kernel<RR, KK, false>), dim3((unsigned)tiles), dim3(256), 0,\
+                               s, xp, rows, cols, nseg, a, b, f, c, k);                            \
+    } while (0)
 #define TL_KIND(RR)                                                                                \
     switch (kind) {                                                                                \
     case 0: TL(RR, 0); break;                                                                      \
