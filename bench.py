@@ -11,10 +11,11 @@ resident in HBM.  Prints one JSON line.
 Steps cycle through BATCHES resident batches, each with its own outputs
 (distinct HBM addresses, 2.8 GB in all), so no step finds its input in the
 256 MB Infinity Cache that the previous step just streamed through: the
-timed rate is an HBM rate.  Every other workload is timed the same way, over
-enough copies of its inputs that at least 1 GB of other inputs is read between
-two reads of the same one (a kernel whose input is small, such as a
-dequantization, gets more copies).
+timed rate is an HBM rate.  The act_16384 breakdown workloads use the same
+batches; every other workload is timed over enough copies of its inputs that
+at least 1 GB of other inputs is read between two reads of the same one (a
+kernel whose input is small, such as a dequantization, gets more copies), and
+the codes a dequantizer reads are written into every copy before timing.
 
 Besides the timed steps it reports, in the same line:
   roofline      the one-pass kernel's achieved GB/s (HIP events on the stream
@@ -24,10 +25,10 @@ Besides the timed steps it reports, in the same line:
                 matches the kernel source
   ceilings      per read:write mix (read, write, copy, row-wise quantize,
                 one-pass, dequantize, FP4 encode, FP4 dequantize, FP8 block to
-                MXFP8), the best
-                rate of several trivial-arithmetic
-                streaming patterns (bench_streams.hip) over the same cold
-                batches; ceiling_runs lists every pattern's rate
+                MXFP8), the best rate of several trivial-arithmetic streaming
+                patterns (bench_streams.hip: the quantizers' tiles in the plain
+                and the XCD row-block order, and grid-stride walks) over cold
+                inputs; ceiling_runs lists every pattern's rate
   cpu_baseline  the CPU oracle (single-threaded C) timed on a bounded sample
                 of the same workload, and the same sharded over host threads
   breakdown     every other quantizer workload (row-wise weight, grouped MoE
