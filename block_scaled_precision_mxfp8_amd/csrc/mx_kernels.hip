@@ -145,12 +145,13 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
 
 // ---------------------------------------------------------------------------
 // Body of the transposed column-wise kernel (+ row-wise + fake-quant), one
-// read of x.  A wave holds one 32-row group x 512 columns in registers (32 x
-// 16 bytes per lane): the column amax is an in-lane max over the 32 loads, the
-// row amax a quad max per row.  Column codes go through the hardware convert
-// two rows at a time (the pair it converts must share one scale, i.e. one
-// column).  (The x-layout column-wise kernel, mx_colwise_kernel, splits each
-// group over several waves instead.)
+// read of x.  A wave holds one 32-row group x 256 columns in registers (32 x
+// 8 bytes per lane, 4 columns each): the column amax is an in-lane max over
+// the 32 loads, the row amax a max over the 8 lanes of a 32-element group.
+// Column codes go through the hardware convert two rows at a time (the pair
+// it converts must share one scale, i.e. one column).  (The x-layout
+// column-wise kernel, mx_colwise_kernel, splits each group over several
+// waves instead.)
 // ---------------------------------------------------------------------------
 // Column codes go to the transposed layout: staged in LDS as
 // lds_t[column slot][row] (column slot j*64 + lane for the lane's column j,
@@ -158,48 +159,51 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
 // qt; the column scales are staged after them, one dword (the workgroup's 4
 // groups) per column, for st [cols, nrg].
 constexpr int kTPitch = 33;  // dwords per LDS column slot: 128 rows of codes + 1 (no bank conflicts)
+constexpr int kSegT = 256;   // columns per transposed workgroup tile (64 lanes x 4)
+
+// Max over the 8 lanes of one 32-element row group (4 columns per lane).
+__device__ __forceinline__ uint32_t oct_max(uint32_t v)
+{
+    v = max(v, dpp_swap1(v));
+    v = max(v, dpp_swap2(v));
+    return max(v, (uint32_t)__shfl_xor((int)v, 4, kWave));
+}
 
 template <bool kRow, bool kFQRow, bool kFull>
 __device__ __forceinline__ void mx_colwise_t_body(const uint16_t *__restrict__ x, int64_t rows,
-                                                  int64_t cols, uint8_t *__restrict__ qr,
-                                                  uint8_t *__restrict__ sr,
-                                                  uint16_t *__restrict__ fq_row, int64_t g,
-                                                  int64_t col, uint32_t *__restrict__ lds_t)
+                                                   int64_t cols, uint8_t *__restrict__ qr,
+                                                   uint8_t *__restrict__ sr,
+                                                   uint16_t *__restrict__ fq_row, int64_t g,
+                                                   int64_t col, uint32_t *__restrict__ lds_t)
 {
     constexpr bool kRowAny = kRow || kFQRow;
     const bool cin = kFull || col < cols;
     const int64_t r0 = g * 32;
     const int64_t ngr = cols >> 5;
-
-    uint4 v[32];
+    uint2 v[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (kFull || (cin && r0 + i < rows))
-            v[i] = ld16<kNTLoad>(x + (r0 + i) * cols + col);
+        v[i] = make_uint2(0, 0);
+        if (kFull || (cin && r0 + i < rows)) v[i] = ld8<kNTLoad>(x + (r0 + i) * cols + col);
     }
-
-    // column scales: in-lane amax over the 32 rows, one E8M0 byte per column
-    uint32_t s[8];
-    bool nan[8];
-    uint32_t lim2[4];
-    float sf[8];
-    int e[8];
+    uint32_t s[4];
+    bool nan[4];
+    uint32_t lim2[2];
+    float sf[4];
+    int e[4];
     bool col_slow;
     {
-        uint32_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+        // column scales: in-lane amax over the 32 rows, one E8M0 byte per column
+        uint32_t m0 = 0, m1 = 0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
             m0 = pk_max_u16(m0, mag2(v[i].x));
             m1 = pk_max_u16(m1, mag2(v[i].y));
-            m2 = pk_max_u16(m2, mag2(v[i].z));
-            m3 = pk_max_u16(m3, mag2(v[i].w));
         }
-        const uint32_t am[8] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16,
-                                m2 & 0xFFFFu, m2 >> 16, m3 & 0xFFFFu, m3 >> 16};
+        const uint32_t am[4] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16};
         bool any_nan = false;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             s[j] = mx_scale_byte(am[j]);
             nan[j] = s[j] == 0xFFu;
             any_nan |= nan[j];
@@ -207,112 +211,83 @@ __device__ __forceinline__ void mx_colwise_t_body(const uint16_t *__restrict__ x
             e[j] = 7 - (int)s[j];
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < 2; ++k)
             lim2[k] = mx_limit_bf16(s[2 * k]) | (mx_limit_bf16(s[2 * k + 1]) << 16);
         if (cin) {
             // byte `wave` of the column's dword: the workgroup's 4 groups of it
-            uint8_t *lds_s = reinterpret_cast<uint8_t *>(lds_t + kSeg * kTPitch);
+            uint8_t *lds_s = reinterpret_cast<uint8_t *>(lds_t + kSegT * kTPitch);
             const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
             const int ln = threadIdx.x & (kWave - 1);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) lds_s[(ln * 8 + j) * 4 + wv] = (uint8_t)s[j];
+            for (int j = 0; j < 4; ++j) lds_s[(ln * 4 + j) * 4 + wv] = (uint8_t)s[j];
         }
         col_slow = wave_any(any_nan);  // a NaN/Inf column in the wave: exact software path
     }
-
-    // one row's row-wise codes and scale byte (do_q) and fake-quant (do_fq) out
-    auto row_work = [&](int i, bool do_q, bool do_fq) __attribute__((always_inline)) {
-        const int64_t r = r0 + i;
-        const bool ok = kFull || (cin && r < rows);
-        const MxRow8 m = mx_row_encode8(v[i]);
-        const bool nan_group = m.s == 0xFFu;
-        if (do_q && ok) {
-            st8<kNTStore>(qr + r * cols + col, make_uint2(m.c0, m.c1));
-            sr[r * ngr + (col >> 5)] = (uint8_t)m.s;  // same byte from the 4 lanes of a quad
-        }
-        if (do_fq) {
-            uint2 lo, hi;
-            if (wave_any(nan_group)) {  // rare: a NaN/Inf group in this row of the wave
-                lo = mx_dequant4(m.c0, (int)m.s - 7, nan_group);
-                hi = mx_dequant4(m.c1, (int)m.s - 7, nan_group);
-            } else {
-                lo = mx_dequant4_hw(m.c0, m.sf);
-                hi = mx_dequant4_hw(m.c1, m.sf);
-            }
-            if (ok)
-                st16<kNTStore>(fq_row + r * cols + col, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        }
-    };
-
     // codes of rows i-2, i-1 wait here until rows i, i+1 complete a 4-row
     // dword per column
-    uint32_t tq[4] = {0u, 0u, 0u, 0u};
+    uint32_t tq0 = 0u, tq1 = 0u;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-
     static_for<0, 32, 2>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
-        {
-            uint32_t a0, a1, b0, b1;  // rows i and i+1: columns 0-3 and 4-7 of the lane
-            if (!col_slow) {
-                // the pair fed to one convert shares a scale: same column, rows i and i+1
-                const uint32_t a[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-                const uint32_t b[4] = {v[i + 1].x, v[i + 1].y, v[i + 1].z, v[i + 1].w};
-                uint32_t rp[4];
+        uint32_t a0, b0;  // rows i and i+1, the lane's 4 columns
+        if (!col_slow) {
+            // the pair fed to one convert shares a scale: same column, rows i and i+1
+            const uint32_t rp0 = e4m3_colpair_hw(clamp_mag2(v[i].x, lim2[0]),
+                                                 clamp_mag2(v[i + 1].x, lim2[0]), sf[0], sf[1]);
+            const uint32_t rp1 = e4m3_colpair_hw(clamp_mag2(v[i].y, lim2[1]),
+                                                 clamp_mag2(v[i + 1].y, lim2[1]), sf[2], sf[3]);
+            a0 = __builtin_amdgcn_perm(rp1, rp0, 0x06040200u);
+            b0 = __builtin_amdgcn_perm(rp1, rp0, 0x07050301u);
+        } else {
+            a0 = e4m3x4_col(v[i].x, v[i].y, e[0], e[1], e[2], e[3], nan[0], nan[1], nan[2], nan[3]);
+            b0 = e4m3x4_col(v[i + 1].x, v[i + 1].y, e[0], e[1], e[2], e[3], nan[0], nan[1], nan[2],
+                            nan[3]);
+        }
+        if (i % 4 == 0) {
+            tq0 = a0;
+            tq1 = b0;
+        } else {
+            // 4x4 byte transpose: rows i-2..i+1 x the lane's 4 columns -> one
+            // dword (4 consecutive rows) per column
+            const uint32_t lo01 = __builtin_amdgcn_perm(tq1, tq0, 0x05010400u);
+            const uint32_t hi01 = __builtin_amdgcn_perm(tq1, tq0, 0x07030602u);
+            const uint32_t lo23 = __builtin_amdgcn_perm(b0, a0, 0x05010400u);
+            const uint32_t hi23 = __builtin_amdgcn_perm(b0, a0, 0x07030602u);
+            const uint32_t cw[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                                    __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                                    __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                                    __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    rp[k] = e4m3_colpair_hw(clamp_mag2(a[k], lim2[k]), clamp_mag2(b[k], lim2[k]),
-                                            sf[2 * k], sf[2 * k + 1]);
-                a0 = __builtin_amdgcn_perm(rp[1], rp[0], 0x06040200u);
-                a1 = __builtin_amdgcn_perm(rp[3], rp[2], 0x06040200u);
-                b0 = __builtin_amdgcn_perm(rp[1], rp[0], 0x07050301u);
-                b1 = __builtin_amdgcn_perm(rp[3], rp[2], 0x07050301u);
-            } else {
-                a0 = e4m3x4_col(v[i].x, v[i].y, e[0], e[1], e[2], e[3], nan[0], nan[1], nan[2],
-                                nan[3]);
-                a1 = e4m3x4_col(v[i].z, v[i].w, e[4], e[5], e[6], e[7], nan[4], nan[5], nan[6],
-                                nan[7]);
-                b0 = e4m3x4_col(v[i + 1].x, v[i + 1].y, e[0], e[1], e[2], e[3], nan[0], nan[1],
-                                nan[2], nan[3]);
-                b1 = e4m3x4_col(v[i + 1].z, v[i + 1].w, e[4], e[5], e[6], e[7], nan[4], nan[5],
-                                nan[6], nan[7]);
-            }
-            {
-                if (i % 4 == 0) {
-                    tq[0] = a0; tq[1] = a1; tq[2] = b0; tq[3] = b1;
-                } else {
-                    // 4x4 byte transposes: rows i-2..i+1 x columns -> one dword
-                    // (4 consecutive rows) per column
-                    uint32_t cw[8];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t w0 = tq[h], w1 = tq[2 + h], w2 = h ? a1 : a0,
-                                       w3 = h ? b1 : b0;
-                        const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
-                        const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
-                        const uint32_t lo23 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
-                        const uint32_t hi23 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
-                        cw[4 * h + 0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
-                        cw[4 * h + 1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
-                        cw[4 * h + 2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
-                        cw[4 * h + 3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        lds_t[(j * kWave + lane) * kTPitch + wave * 8 + i / 4] = cw[j];
-                }
-            }
+            for (int j = 0; j < 4; ++j)
+                lds_t[(j * kWave + lane) * kTPitch + wave * 8 + i / 4] = cw[j];
         }
     });
-    // then the row-wise work: one stream after the other measured 2.4% faster
-    // on MI355X than interleaving the column and row outputs row by row
-    static_for<0, 32, 2>([&](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        if (kRowAny) {
-            row_work(i, kRow, kFQRow);
-            row_work(i + 1, kRow, kFQRow);
+    // then the row-wise work, row by row: a group of 32 is 8 lanes, each with
+    // one dword of 4 codes
+    if (kRowAny) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int64_t r = r0 + i;
+            const bool ok = kFull || (cin && r < rows);
+            const uint32_t am = pk_max_u16(mag2(v[i].x), mag2(v[i].y));
+            const uint32_t sb = mx_scale_byte(oct_max(max(am & 0xFFFFu, am >> 16)));
+            const uint32_t lim = mx_limit_bf16(sb);
+            const float rsf = e8m0_to_f32(sb);
+            uint32_t c = e4m3x4_row_hw(v[i].x, v[i].y, lim | (lim << 16), rsf);
+            const bool nan_group = sb == 0xFFu;
+            if (nan_group) c = 0x7F7F7F7Fu | signs4(v[i].x, v[i].y);
+            if (kRow && ok) {
+                st4<kNTStore>(qr + r * cols + col, c);
+                sr[r * ngr + (col >> 5)] = (uint8_t)sb;  // same byte from the group's 8 lanes
+            }
+            if (kFQRow) {  // a NaN/Inf group in this row of the wave: exact software path
+                const uint2 d = wave_any(nan_group) ? mx_dequant4(c, (int)sb - 7, nan_group)
+                                                    : mx_dequant4_hw(c, rsf);
+                if (ok) st8<kNTStore>(fq_row + r * cols + col, d);
+            }
         }
-    });
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -493,16 +468,20 @@ __global__ __launch_bounds__(64 * kW) void mx_colwise_kernel(
 
 // ---------------------------------------------------------------------------
 // Column-wise in the transposed layout (+ optional row-wise and fake-quant),
-// one read of x.  The four waves of a workgroup quantize 128 rows x 512
+// one read of x.  The four waves of a workgroup quantize 128 rows x 256
 // columns (mx_colwise_t_body, one 32-row group each), staging the column
-// codes and scales in LDS; after a
-// barrier the workgroup writes them out: column c's 128 codes are 128
-// contiguous bytes of qt (8 lanes, 16-byte stores) and its 4 scales one
-// dword of st.  Measured on MI355X against alternatives (cold [16384, 7168]
-// input, column codes only): codes stored straight from registers, 16-byte
+// codes and scales in LDS; after a barrier the workgroup writes them out:
+// column c's 128 codes are 128 contiguous bytes of qt (8 lanes, 16-byte
+// stores) and its 4 scales one dword of st.  Measured on MI355X against
+// alternatives (cold [16384, 7168] input): 4 columns per lane (256-column
+// tiles, 156 VGPRs, 3 waves per SIMD) ran 4% faster than 8 per lane
+// (512-column tiles, 2 waves per SIMD) both column-only and in one pass --
+// after its loads a wave converts half as much before the barrier; with a
+// 128-VGPR cap (4 waves per SIMD) the one pass gained nothing.  For column
+// codes only, earlier forms: codes stored straight from registers, 16-byte
 // pieces of 64 lines per instruction, 3.1 TB/s (1.4 with streaming stores);
-// scale bytes stored straight from registers 4.67 TB/s; this form 4.87; a
-// persistent workgroup prefetching its next tile spills registers, 4.0.
+// scale bytes stored straight from registers 4.67 TB/s; a persistent
+// workgroup loading its next tile while writing one out was 3-5% slower.
 // ---------------------------------------------------------------------------
 // Workgroup order.  A line of st (128 groups of one column) collects 4 bytes
 // from each of 32 workgroups: the 32 row bands of one segment.  Column-only
@@ -514,12 +493,12 @@ template <bool kRow, bool kFQRow>
 constexpr bool kColTUnits = !kRow && !kFQRow;
 
 template <bool kRow, bool kFQRow>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mx_colwise_t_kernel(
+__global__ __launch_bounds__(256) void mx_colwise_t_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qt,
     int64_t ldt, uint8_t *__restrict__ st, uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
     uint16_t *__restrict__ fq_row, int64_t nseg)
 {
-    __shared__ uint32_t lds_t[kSeg * kTPitch + kSeg];
+    __shared__ uint32_t lds_t[kSegT * kTPitch + kSegT];
     int64_t seg, rb;
     if (kColTUnits<kRow, kFQRow>) {
         // workgroups in units of 32 consecutive row bands of one segment,
@@ -537,11 +516,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     }
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-    const int64_t col = seg * kSeg + lane * 8;
-    const int64_t g = rb * (kColTileRows / 32) + wave;  // 32-row group index
+    const int64_t col = seg * kSegT + lane * 4;
+    const int64_t g = rb * (kColTileRows / 32) + wave;
     const int64_t nrg = (rows + 31) / 32;
     if (g * 32 < rows) {  // wave-uniform; every wave reaches the barrier below
-        if ((seg + 1) * kSeg <= cols && g * 32 + 32 <= rows)
+        if ((seg + 1) * kSegT <= cols && g * 32 + 32 <= rows)
             mx_colwise_t_body<kRow, kFQRow, true>(x, rows, cols, qr, sr, fq_row, g, col, lds_t);
         else
             mx_colwise_t_body<kRow, kFQRow, false>(x, rows, cols, qr, sr, fq_row, g, col, lds_t);
@@ -550,10 +529,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     {
         // scales: the tile's 4 groups of each column, one dword when st rows
         // are dword-aligned (nrg % 4 == 0; st itself is 4-byte aligned)
-        const uint32_t *lds_s = lds_t + kSeg * kTPitch;
+        const uint32_t *lds_s = lds_t + kSegT * kTPitch;
         const int64_t g0 = rb * 4;
-        for (int cl = threadIdx.x; cl < kSeg; cl += 256) {
-            const int64_t c = seg * kSeg + cl;
+        for (int cl = threadIdx.x; cl < kSegT; cl += 256) {
+            const int64_t c = seg * kSegT + cl;
             if (c >= cols) continue;
             const uint32_t w4 = lds_s[cl];
             if (g0 + 4 <= nrg && (nrg & 3) == 0) {
@@ -564,15 +543,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
             }
         }
     }
-    // write-out: LDS slot ridx holds column (ridx % 64) * 8 + ridx / 64 of the
-    // segment; 8 threads per slot, 16 rows (one dword quad) each.  Rows and
+    // write-out: LDS slot ridx holds column (ridx % 64) * 4 + ridx / 64 of the
+    // tile; 8 threads per slot, 16 rows (one dword quad) each.  Rows and
     // columns past the tensor's edge hold codes of nothing and are skipped.
     const int k = threadIdx.x & 7;
     const int64_t r = rb * kColTileRows + k * 16;
 #pragma unroll 4
-    for (int it = 0; it < kSeg / 32; ++it) {
+    for (int it = 0; it < kSegT / 32; ++it) {
         const int ridx = it * 32 + (threadIdx.x >> 3);
-        const int64_t c = seg * kSeg + (ridx & (kWave - 1)) * 8 + (ridx >> 6);
+        const int64_t c = seg * kSegT + (ridx & (kWave - 1)) * 4 + (ridx >> 6);
         const uint32_t *src = lds_t + ridx * kTPitch + k * 4;
         const uint4 w = make_uint4(src[0], src[1], src[2], src[3]);
         if (c >= cols || r >= rows) continue;
@@ -785,7 +764,7 @@ hipError_t launch_mx_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, ui
                                int64_t ldt, uint8_t *st, uint8_t *qr, uint8_t *sr,
                                uint16_t *fq_row, hipStream_t stream)
 {
-    const int64_t nseg = (cols + kSeg - 1) / kSeg;
+    const int64_t nseg = (cols + kSegT - 1) / kSegT;
     const int64_t nrb = (rows + kColTileRows - 1) / kColTileRows;
     if (nseg <= 0 || nrb <= 0) return hipSuccess;
     // column-only: 32-band units spread over the 8 XCDs (kColTUnits)
