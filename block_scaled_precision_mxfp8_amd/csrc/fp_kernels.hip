@@ -85,18 +85,21 @@ __device__ __forceinline__ uint2 bfp8_encode8(uint4 v, float div, float y, bool 
 }
 
 // ---------------------------------------------------------------------------
-// Block-FP8: one workgroup per 128 x 128 tile.  Thread t loads 8 rows
-// (t/16 + 16k) x 8 columns ((t%16)*8): each wave load covers 4 rows x 256 B.
+// Block-FP8: one workgroup of 8 waves per 128 x 128 tile.  Thread t loads 4
+// rows (t/16 + 32k) x 8 columns ((t%16)*8): each wave load covers 4 rows x
+// 256 B.  8 waves of 16 rows measured 5% faster on MI355X than 4 waves of 32
+// ([8192, 8192], cold): after the tile's barrier each wave encodes half as
+// much; 16 waves of 8 rows were 7% slower.
 // A stack of slices [G, rows, cols] (ts tiles each) is quantized slice by
 // slice: no tile crosses a slice boundary.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(512) void bfp8_quant_kernel(const uint16_t *__restrict__ x,
                                                          int64_t rows, int64_t cols,
                                                          uint8_t *__restrict__ q,
                                                          float *__restrict__ scale, int64_t tc,
                                                          int64_t ts)
 {
-    __shared__ uint32_t red[4];
+    __shared__ uint32_t red[8];
     const int64_t slice = blockIdx.x / ts, t = blockIdx.x % ts;
     x += slice * rows * cols;
     q += slice * rows * cols;
@@ -107,11 +110,11 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
     const int64_t rbase = bi * kBlk + (tid >> 4);
     const bool cin = col < cols;  // cols % 8 == 0: a chunk is all in or all out
 
-    uint4 v[8];
+    uint4 v[4];
     uint32_t m = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int64_t r = rbase + 16 * k;
+    for (int k = 0; k < 4; ++k) {
+        const int64_t r = rbase + 32 * k;
         v[k] = make_uint4(0, 0, 0, 0);
         if (cin && r < rows) v[k] = ld16<kNTLoad>(x + r * cols + col);
         m = max(m, amax8(v[k]));
@@ -119,7 +122,9 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
     m = wave_max(m);
     if ((tid & (kWave - 1)) == 0) red[tid / kWave] = m;
     __syncthreads();
-    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    m = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) m = max(m, red[w]);
 
     const bool nonfinite = m >= 0x7F80u;
     const float A = __uint_as_float(m << 16);      // exact: amax is a bf16 value
@@ -133,8 +138,8 @@ __global__ __launch_bounds__(256) void bfp8_quant_kernel(const uint16_t *__restr
     const bool fast = !nonfinite && markstein_ok(div);
     const float y = fast ? 1.0f / div : 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int64_t r = rbase + 16 * k;
+    for (int k = 0; k < 4; ++k) {
+        const int64_t r = rbase + 32 * k;
         const uint2 c = bfp8_encode8(v[k], div, y, fast, nonfinite);
         if (cin && r < rows) st8<kNTStore>(q + r * cols + col, c);
     }
@@ -727,7 +732,7 @@ hipError_t launch_bfp8_quant(const uint16_t *x, int64_t slices, int64_t rows, in
     const int64_t ts = tr * tc;
     if (ts <= 0 || slices <= 0) return hipSuccess;
     if (ts > 0x7FFFFFFF / slices) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bfp8_quant_kernel, dim3((unsigned)(ts * slices)), dim3(256), 0, stream, x,
+    hipLaunchKernelGGL(bfp8_quant_kernel, dim3((unsigned)(ts * slices)), dim3(512), 0, stream, x,
                        rows, cols, q, scale, tc, ts);
     return hipGetLastError();
 }
