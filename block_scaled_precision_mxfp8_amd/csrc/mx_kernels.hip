@@ -488,7 +488,8 @@ __global__ __launch_bounds__(64 * kW) void mx_colwise_kernel(
 // launches run those 32 back to back on one XCD, so the pieces merge in that
 // XCD's L2 before write-back: on MI355X this removed the +9.7% of extra HBM
 // writes and took [16384, 7168] from 73.6 to 68.1 us.  With the row-wise
-// outputs as well, the plain segment-fastest order measured 1-2% faster.
+// outputs as well, the plain segment-fastest order measured 1-3% faster than
+// a row block's segments on one XCD, with 512- and with 256-column tiles.
 template <bool kRow, bool kFQRow>
 constexpr bool kColTUnits = !kRow && !kFQRow;
 
