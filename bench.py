@@ -34,7 +34,10 @@ Besides the timed steps it reports, in the same line:
   breakdown     every other quantizer workload (row-wise weight, grouped MoE
                 experts, block-FP8, NVFP4, dequantizers), each timed on its own;
                 the quantizers and dequantizers also as a fraction of their
-                mix's ceiling (measured on the [16384, 7168] batches)
+                mix's ceiling (measured on the [16384, 7168] batches); the
+                [8192, 8192] kernels also against the streams measured on
+                their own buffers (ceilings_square_8192), NVFP4 quantize
+                against its read-only and FP4-encode streams back to back
 """
 from __future__ import annotations
 
@@ -400,6 +403,7 @@ def main():
     # breakdown: every other workload, timed on its own
     # ------------------------------------------------------------------
     breakdown = {}
+    sq_ceilings = None
     if not args.no_breakdown:
         def rotated(launches, nbytes, iters=20, mix=None):
             """Back-to-back launches cycling through copies with their own
@@ -628,7 +632,29 @@ def main():
             [lambda d=d: check(lib.nvfp4_dequantize(P(d["nq"]), P(d["ns"]), P(d["ng"]), n_, n_,
                                                     P(d["bd"]), sp), "nvfp4 dq") for d in ysets],
             nbytes, mix="fp4dq")
-        del ysets
+        # the same streams on the square_8192 buffers, run last since they
+        # overwrite codes: the square kernels also stand against ceilings
+        # measured at their own size (about half the bytes per launch of the
+        # act_16384 streams, so ramp-up and drain weigh the same for both)
+        sq_batches = [{"x": d["y"], "qc": d["bq"], "qr": d["rq8"], "fq": d["bd"], "sr": d["rs8"]}
+                      for d in ysets[:ncopies(2 * ye)]]
+        sq_ceilings, _ = measure_ceilings(load_streams(), sq_batches, n_, n_, stream, sp)
+        for key, mix in (("square_8192 block-FP8 quantize", "row"),
+                         ("square_8192 block-FP8 dequantize", "dequant"),
+                         ("square_8192 block-FP8 -> MXFP8 re-quantize (one pass)", "requant"),
+                         ("square_8192 NVFP4 dequantize", "fp4dq")):
+            r = breakdown[key]
+            r["ceiling_same_size_mix"] = mix
+            r["frac_ceiling_same_size"] = round(r["GB/s"] / sq_ceilings[mix]["GB/s"], 4)
+        # NVFP4 quantize: its amax pass reads x (the read-only mix), its
+        # encoding pass reads x again and writes codes and scales (the FP4
+        # encode mix); the two streams back to back bound the pair of passes
+        r = breakdown["square_8192 NVFP4 quantize (unique bytes)"]
+        two = (2 * ye / sq_ceilings["read"]["GB/s"] + (2 * ye + ye // 2 + ye // 16)
+               / sq_ceilings["fp4"]["GB/s"]) / 1e3
+        r["two_stream_us"] = round(two, 2)
+        r["frac_two_stream"] = round(two / r["us"], 4)
+        del ysets, sq_batches
 
     out = {
         "metric": METRIC,
@@ -653,6 +679,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ceilings": ceilings,
+        "ceilings_square_8192": sq_ceilings,
         "ceiling_runs": ceiling_runs,
         "breakdown": breakdown,
         "device": torch.cuda.get_device_name(dev),
