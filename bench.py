@@ -156,7 +156,7 @@ MIX_DESC = {
     "fp4dq": "1/2 + 1/32 B read : 2 written", "requant": "1 B read : 1 + 1/32 written"}
 
 
-def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
+def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20, mixes=None):
     """Best GB/s per mix over the tiled (R = 1, 2, 4, 8 rows per wave; plain or
     XCD row-block order) and flat
     (U = 2, 4, 8 vectors in flight; 1024, 2048, 4096 workgroups) patterns,
@@ -202,6 +202,8 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
     for v in range(8 * len(MIXES)):
         mix, R = MIXES[(v // 4) % len(MIXES)], 1 << (v % 4)
         order = " xcd" if v >= 4 * len(MIXES) else ""
+        if mixes is not None and mix not in mixes:
+            continue
 
         def go(a, v=v):
             st = L.bench_stream_tiled(v, a[0], rows, cols, a[1], a[2], a[3], a[4], A(sink), sp)
@@ -210,6 +212,8 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20):
         runs[f"{mix} tiled R{R}{order}"] = (mix, MIX_BYTES[mix][0] * e / timed(go, sources[mix]) / 1e9)
     for v in range(3 * len(MIXES)):
         mix, U = MIXES[v // 3], (2, 4, 8)[v % 3]
+        if mixes is not None and mix not in mixes:
+            continue
         for grid in (1024, 2048, 4096):
             def go(a, v=v, grid=grid):
                 st = L.bench_stream_flat(v, a[0], e // 8, a[1], a[2], a[3], A(sink), grid, sp)
@@ -403,7 +407,7 @@ def main():
     # breakdown: every other workload, timed on its own
     # ------------------------------------------------------------------
     breakdown = {}
-    sq_ceilings = None
+    sq_ceilings = sq_ceilings_weight = None
     if not args.no_breakdown:
         def rotated(launches, nbytes, iters=20, mix=None):
             """Back-to-back launches cycling through copies with their own
@@ -516,6 +520,15 @@ def main():
             [lambda t=t: check(lib.mxq_quantize_rowwise(P(t[0]), wr, wc, wc, P(t[1]), wc, P(t[2]),
                                                         wc // 32, None, 0, sp), "rowwise")
              for t in wsets], wbytes, mix="row")
+        # the row-wise mix's streams on these buffers (the codes buffer stands
+        # in for the planes that mix does not write)
+        wc_ceil, _ = measure_ceilings(load_streams(), [{"x": t[0], "qc": t[1], "qr": t[1], "fq": t[1],
+                                                        "sr": t[2]} for t in wsets],
+                                      wr, wc, stream, sp, mixes=("row",))
+        breakdown["weight_4097 row-wise"]["ceiling_same_size_mix"] = "row"
+        breakdown["weight_4097 row-wise"]["frac_ceiling_same_size"] = round(
+            breakdown["weight_4097 row-wise"]["GB/s"] / wc_ceil["row"]["GB/s"], 4)
+        sq_ceilings_weight = wc_ceil
         del w0, wsets
 
         # mx_small row-wise + dequantize: a latency measurement (the data is
@@ -680,6 +693,7 @@ def main():
         "cpu_baseline": cpu,
         "ceilings": ceilings,
         "ceilings_square_8192": sq_ceilings,
+        "ceilings_weight_4097": sq_ceilings_weight,
         "ceiling_runs": ceiling_runs,
         "breakdown": breakdown,
         "device": torch.cuda.get_device_name(dev),
