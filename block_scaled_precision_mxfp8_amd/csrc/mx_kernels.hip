@@ -145,13 +145,12 @@ __global__ __launch_bounds__(256) void mx_rowwise_kernel(const uint16_t *__restr
 
 // ---------------------------------------------------------------------------
 // Body of the transposed column-wise kernel (+ row-wise + fake-quant), one
-// read of x.  A wave holds one 32-row group x 256 columns in registers (32 x
-// 8 bytes per lane, 4 columns each): the column amax is an in-lane max over
-// the 32 loads, the row amax a max over the 8 lanes of a 32-element group.
-// Column codes go through the hardware convert two rows at a time (the pair
-// it converts must share one scale, i.e. one column).  (The x-layout
-// column-wise kernel, mx_colwise_kernel, splits each group over several
-// waves instead.)
+// read of x.  Two waves hold one 32-row group x 256 columns in registers,
+// 16 rows each (16 x 8 bytes per lane, 4 columns each): the column amax is an
+// in-lane max over a wave's 16 loads, combined with the other half's through
+// LDS behind one barrier; the row amax is a max over the 8 lanes of a
+// 32-element group.  Column codes go through the hardware convert two rows
+// at a time (the pair it converts must share one scale, i.e. one column).
 // ---------------------------------------------------------------------------
 // Column codes go to the transposed layout: staged in LDS as
 // lds_t[column slot][row] (column slot j*64 + lane for the lane's column j,
@@ -174,18 +173,36 @@ __device__ __forceinline__ void mx_colwise_t_body(const uint16_t *__restrict__ x
                                                    int64_t cols, uint8_t *__restrict__ qr,
                                                    uint8_t *__restrict__ sr,
                                                    uint16_t *__restrict__ fq_row, int64_t g,
-                                                   int64_t col, uint32_t *__restrict__ lds_t)
+                                                   int half, int64_t col,
+                                                   uint32_t *__restrict__ lds_t,
+                                                   uint2 *__restrict__ xm, bool active)
 {
     constexpr bool kRowAny = kRow || kFQRow;
     const bool cin = kFull || col < cols;
-    const int64_t r0 = g * 32;
+    const int64_t r0 = g * 32 + half * 16;
     const int64_t ngr = cols >> 5;
-    uint2 v[32];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    uint2 v[16];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16; ++i) {
         v[i] = make_uint2(0, 0);
-        if (kFull || (cin && r0 + i < rows)) v[i] = ld8<kNTLoad>(x + (r0 + i) * cols + col);
+        if (active && (kFull || (cin && r0 + i < rows))) v[i] = ld8<kNTLoad>(x + (r0 + i) * cols + col);
     }
+    // column scales: in-lane amax over this half's 16 rows, then the other
+    // half's (the partner wave, wave ^ 1) through LDS
+    uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        m0 = pk_max_u16(m0, mag2(v[i].x));
+        m1 = pk_max_u16(m1, mag2(v[i].y));
+    }
+    xm[wave * kWave + lane] = make_uint2(m0, m1);
+    __syncthreads();
+    const uint2 o = xm[(wave ^ 1) * kWave + lane];
+    m0 = pk_max_u16(m0, o.x);
+    m1 = pk_max_u16(m1, o.y);
+    if (!active) return;  // wave-uniform: a group past the last row (after the barrier)
     uint32_t s[4];
     bool nan[4];
     uint32_t lim2[2];
@@ -193,13 +210,6 @@ __device__ __forceinline__ void mx_colwise_t_body(const uint16_t *__restrict__ x
     int e[4];
     bool col_slow;
     {
-        // column scales: in-lane amax over the 32 rows, one E8M0 byte per column
-        uint32_t m0 = 0, m1 = 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            m0 = pk_max_u16(m0, mag2(v[i].x));
-            m1 = pk_max_u16(m1, mag2(v[i].y));
-        }
         const uint32_t am[4] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16};
         bool any_nan = false;
 #pragma unroll
@@ -213,22 +223,20 @@ __device__ __forceinline__ void mx_colwise_t_body(const uint16_t *__restrict__ x
 #pragma unroll
         for (int k = 0; k < 2; ++k)
             lim2[k] = mx_limit_bf16(s[2 * k]) | (mx_limit_bf16(s[2 * k + 1]) << 16);
-        if (cin) {
-            // byte `wave` of the column's dword: the workgroup's 4 groups of it
+        if (cin && half == 0) {
+            // byte `group` of the column's dword: the workgroup's 4 groups of it
             uint8_t *lds_s = reinterpret_cast<uint8_t *>(lds_t + kSegT * kTPitch);
-            const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-            const int ln = threadIdx.x & (kWave - 1);
+            const int gl = wave >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) lds_s[(ln * 4 + j) * 4 + wv] = (uint8_t)s[j];
+            for (int j = 0; j < 4; ++j) lds_s[(lane * 4 + j) * 4 + gl] = (uint8_t)s[j];
         }
         col_slow = wave_any(any_nan);  // a NaN/Inf column in the wave: exact software path
     }
     // codes of rows i-2, i-1 wait here until rows i, i+1 complete a 4-row
     // dword per column
     uint32_t tq0 = 0u, tq1 = 0u;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    static_for<0, 32, 2>([&](auto ic) __attribute__((always_inline)) {
+    const int dw0 = (wave >> 1) * 8 + half * 4;  // first dword of this half's rows in a slot
+    static_for<0, 16, 2>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
         uint32_t a0, b0;  // rows i and i+1, the lane's 4 columns
         if (!col_slow) {
@@ -260,14 +268,14 @@ __device__ __forceinline__ void mx_colwise_t_body(const uint16_t *__restrict__ x
                                     __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                lds_t[(j * kWave + lane) * kTPitch + wave * 8 + i / 4] = cw[j];
+                lds_t[(j * kWave + lane) * kTPitch + dw0 + i / 4] = cw[j];
         }
     });
     // then the row-wise work, row by row: a group of 32 is 8 lanes, each with
     // one dword of 4 codes
     if (kRowAny) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < 16; ++i) {
             const int64_t r = r0 + i;
             const bool ok = kFull || (cin && r < rows);
             const uint32_t am = pk_max_u16(mag2(v[i].x), mag2(v[i].y));
@@ -468,16 +476,18 @@ __global__ __launch_bounds__(64 * kW) void mx_colwise_kernel(
 
 // ---------------------------------------------------------------------------
 // Column-wise in the transposed layout (+ optional row-wise and fake-quant),
-// one read of x.  The four waves of a workgroup quantize 128 rows x 256
-// columns (mx_colwise_t_body, one 32-row group each), staging the column
-// codes and scales in LDS; after a barrier the workgroup writes them out:
+// one read of x.  The eight waves of a workgroup quantize 128 rows x 256
+// columns (mx_colwise_t_body, two waves per 32-row group), staging the
+// column codes and scales in LDS; after a barrier the workgroup writes them out:
 // column c's 128 codes are 128 contiguous bytes of qt (8 lanes, 16-byte
 // stores) and its 4 scales one dword of st.  Measured on MI355X against
 // alternatives (cold [16384, 7168] input): 4 columns per lane (256-column
-// tiles, 156 VGPRs, 3 waves per SIMD) ran 4% faster than 8 per lane
-// (512-column tiles, 2 waves per SIMD) both column-only and in one pass --
-// after its loads a wave converts half as much before the barrier; with a
-// 128-VGPR cap (4 waves per SIMD) the one pass gained nothing.  For column
+// tiles, a wave per group, 156 VGPRs, 3 waves per SIMD) ran 4% faster than 8
+// per lane (512-column tiles, 2 waves per SIMD) both column-only and in one
+// pass -- after its loads a wave converts half as much; splitting each group
+// over two waves of 16 rows (93 VGPRs, two 8-wave workgroups per CU) gained
+// another 1.5% in one pass (135.4 against 137.4 us), within 1% column-only.
+// For column
 // codes only, earlier forms: codes stored straight from registers, 16-byte
 // pieces of 64 lines per instruction, 3.1 TB/s (1.4 with streaming stores);
 // scale bytes stored straight from registers 4.67 TB/s; a persistent
@@ -494,12 +504,13 @@ template <bool kRow, bool kFQRow>
 constexpr bool kColTUnits = !kRow && !kFQRow;
 
 template <bool kRow, bool kFQRow>
-__global__ __launch_bounds__(256) void mx_colwise_t_kernel(
+__global__ __launch_bounds__(512) void mx_colwise_t_kernel(
     const uint16_t *__restrict__ x, int64_t rows, int64_t cols, uint8_t *__restrict__ qt,
     int64_t ldt, uint8_t *__restrict__ st, uint8_t *__restrict__ qr, uint8_t *__restrict__ sr,
     uint16_t *__restrict__ fq_row, int64_t nseg)
 {
     __shared__ uint32_t lds_t[kSegT * kTPitch + kSegT];
+    __shared__ uint2 xm[8 * kWave];  // the two halves' column maxima of each group
     int64_t seg, rb;
     if (kColTUnits<kRow, kFQRow>) {
         // workgroups in units of 32 consecutive row bands of one segment,
@@ -518,13 +529,17 @@ __global__ __launch_bounds__(256) void mx_colwise_t_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int64_t col = seg * kSegT + lane * 4;
-    const int64_t g = rb * (kColTileRows / 32) + wave;
+    const int64_t g = rb * (kColTileRows / 32) + (wave >> 1);  // 32-row group index
+    const int half = wave & 1;                                  // its rows 16*half..16*half+15
     const int64_t nrg = (rows + 31) / 32;
-    if (g * 32 < rows) {  // wave-uniform; every wave reaches the barrier below
+    {
+        const bool active = g * 32 < rows;  // wave-uniform; every wave reaches both barriers
         if ((seg + 1) * kSegT <= cols && g * 32 + 32 <= rows)
-            mx_colwise_t_body<kRow, kFQRow, true>(x, rows, cols, qr, sr, fq_row, g, col, lds_t);
+            mx_colwise_t_body<kRow, kFQRow, true>(x, rows, cols, qr, sr, fq_row, g, half, col,
+                                                  lds_t, xm, active);
         else
-            mx_colwise_t_body<kRow, kFQRow, false>(x, rows, cols, qr, sr, fq_row, g, col, lds_t);
+            mx_colwise_t_body<kRow, kFQRow, false>(x, rows, cols, qr, sr, fq_row, g, half, col,
+                                                   lds_t, xm, active);
     }
     __syncthreads();
     {
@@ -532,7 +547,7 @@ __global__ __launch_bounds__(256) void mx_colwise_t_kernel(
         // are dword-aligned (nrg % 4 == 0; st itself is 4-byte aligned)
         const uint32_t *lds_s = lds_t + kSegT * kTPitch;
         const int64_t g0 = rb * 4;
-        for (int cl = threadIdx.x; cl < kSegT; cl += 256) {
+        for (int cl = threadIdx.x; cl < kSegT; cl += 512) {
             const int64_t c = seg * kSegT + cl;
             if (c >= cols) continue;
             const uint32_t w4 = lds_s[cl];
@@ -550,8 +565,8 @@ __global__ __launch_bounds__(256) void mx_colwise_t_kernel(
     const int k = threadIdx.x & 7;
     const int64_t r = rb * kColTileRows + k * 16;
 #pragma unroll 4
-    for (int it = 0; it < kSegT / 32; ++it) {
-        const int ridx = it * 32 + (threadIdx.x >> 3);
+    for (int it = 0; it < kSegT / 64; ++it) {
+        const int ridx = it * 64 + (threadIdx.x >> 3);
         const int64_t c = seg * kSegT + (ridx & (kWave - 1)) * 4 + (ridx >> 6);
         const uint32_t *src = lds_t + ridx * kTPitch + k * 4;
         const uint4 w = make_uint4(src[0], src[1], src[2], src[3]);
@@ -771,7 +786,7 @@ hipError_t launch_mx_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, ui
     // column-only: 32-band units spread over the 8 XCDs (kColTUnits)
     const int64_t tiles = (qr || fq_row) ? nseg * nrb : 8 * 32 * ((nseg * ((nrb + 31) / 32) + 7) / 8);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)tiles), block(256);
+    const dim3 grid((unsigned)tiles), block(512);
 #define MXQ_COLWISE_T(R, FR)                                                                       \
     hipLaunchKernelGGL((mx_colwise_t_kernel<R, FR>), grid, block, 0, stream, x, rows, cols, qt,    \
                        ldt, st, qr, sr, fq_row, nseg)
