@@ -16,6 +16,10 @@ batches; every other workload is timed over enough copies of its inputs that
 at least 1 GB of other inputs is read between two reads of the same one (a
 kernel whose input is small, such as a dequantization, gets more copies), and
 the codes a dequantizer reads are written into every copy before timing.
+Every timed workload, the streams included, follows an untimed warm-up of at
+least 20 ms (warm_up); the main step follows the streams and its own warm-up
+steps.  Timed right after host-side set-up, the GPU runs slower for a few
+milliseconds: 5-7% on a 50 us kernel after 16 launches, 1% on the main step.
 
 Besides the timed steps it reports, in the same line:
   roofline      the one-pass kernel's achieved GB/s (HIP events on the stream
@@ -156,6 +160,28 @@ MIX_DESC = {
     "fp4dq": "1/2 + 1/32 B read : 2 written", "requant": "1 B read : 1 + 1/32 written"}
 
 
+WARM_S = 0.02  # untimed warm-up before each timed workload, at least this long
+
+
+def warm_up(launch, arg_sets, min_launches=16):
+    """Untimed launches cycling over arg_sets, in rounds of max(min_launches,
+    len(arg_sets)) ended by a synchronize, until WARM_S has passed.  After a
+    pause in GPU work (host-side set-up between workloads) the part takes a
+    few milliseconds to come back to full speed: a 50 us kernel timed after
+    16 launches read 5-7% slower than after 10 ms of launches."""
+    import torch
+    n = max(min_launches, len(arg_sets))
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(n):
+            launch(arg_sets[i % len(arg_sets)])
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARM_S:
+            return
+
+
 def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20, mixes=None):
     """Best GB/s per mix over the tiled (R = 1, 2, 4, 8 rows per wave; plain or
     XCD row-block order) and flat
@@ -187,9 +213,7 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20, mixes=None):
     sources["dequant"], sources["fp4dq"], sources["requant"] = codes1, codes_half, codes_rq
 
     def timed(launch, srcs):
-        for i in range(max(16, len(srcs))):
-            launch(srcs[i % len(srcs)])
-        torch.cuda.synchronize()
+        warm_up(launch, srcs)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for i in range(iters):
@@ -299,6 +323,14 @@ def main():
         check(lib.mxq_quantize_colwise(P(d["x"]), rows, cols, P(d["qc"]), P(d["sc"]), P(d["qr"]),
                                        P(d["sr"]), P(d["fq"]), sp), "mxq_quantize_colwise")
 
+    # Streaming ceilings: per read:write mix, the best of several access
+    # patterns with trivial arithmetic (bench_streams.hip), over the same cold
+    # batches.  The quantizer kernels are reported against the ceiling of
+    # their own mix as well as against the 8 TB/s peak.  Measured before the
+    # main step, so that the step is not timed while the GPU is still coming
+    # back from the host-side set-up above (about 1% on the step).
+    ceilings, ceiling_runs = measure_ceilings(load_streams(), batches, rows, cols, stream, sp)
+
     log(f"warmup {args.warmup}")
     for i in range(max(args.warmup, BATCHES)):
         launch_fused(batches[i % BATCHES])
@@ -341,11 +373,6 @@ def main():
                 "per_launch_us_min_max": [round(min(durs) * 1e3, 2), round(max(durs) * 1e3, 2)]}
     log(f"main: {value:.1f} GB/s per step, kernel {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
 
-    # Streaming ceilings: per read:write mix, the best of several access
-    # patterns with trivial arithmetic (bench_streams.hip), over the same cold
-    # batches.  The quantizer kernels are reported against the ceiling of
-    # their own mix as well as against the 8 TB/s peak.
-    ceilings, ceiling_runs = measure_ceilings(load_streams(), batches, rows, cols, stream, sp)
     oc = ceilings["onepass"]
     roofline["ceiling"] = {"mix": "onepass (2 B read : 4 + 1/16 B written per element)",
                            "GB/s": oc["GB/s"], "pattern": oc["pattern"],
@@ -412,13 +439,11 @@ def main():
         def rotated(launches, nbytes, iters=20, mix=None):
             """Back-to-back launches cycling through copies with their own
             buffers; per-launch time = total / iters.  The untimed warm-up
-            touches every copy and runs at least 16 launches, so that the
-            first workload after the CPU baseline is not timed while the GPU
-            is still leaving its idle clocks.  With `mix`, the result also
-            gives the fraction of that mix's streaming ceiling."""
-            for i in range(max(len(launches), 16)):
-                launches[i % len(launches)]()
-            torch.cuda.synchronize()
+            (warm_up) touches every copy and lasts at least WARM_S, so that no
+            workload is timed while the GPU is still coming back from the
+            host-side set-up before it.  With `mix`, the result also gives the
+            fraction of that mix's streaming ceiling."""
+            warm_up(lambda f: f(), launches)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for i in range(iters):
