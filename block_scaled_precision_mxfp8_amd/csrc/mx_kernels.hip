@@ -487,9 +487,8 @@ __global__ __launch_bounds__(64 * kW) void mx_colwise_kernel(
 // pass -- after its loads a wave converts half as much; splitting each group
 // over two waves of 16 rows (93 VGPRs, two 8-wave workgroups per CU) gained
 // another 1.5% in one pass (135.4 against 137.4 us), within 1% column-only.
-// For column
-// codes only, earlier forms: codes stored straight from registers, 16-byte
-// pieces of 64 lines per instruction, 3.1 TB/s (1.4 with streaming stores);
+// For column codes only, earlier forms: codes stored straight from registers,
+// 16-byte pieces of 64 lines per instruction, 3.1 TB/s (1.4 with streaming stores);
 // scale bytes stored straight from registers 4.67 TB/s; a persistent
 // workgroup loading its next tile while writing one out was 3-5% slower.
 // ---------------------------------------------------------------------------
@@ -499,7 +498,8 @@ __global__ __launch_bounds__(64 * kW) void mx_colwise_kernel(
 // XCD's L2 before write-back: on MI355X this removed the +9.7% of extra HBM
 // writes and took [16384, 7168] from 73.6 to 68.1 us.  With the row-wise
 // outputs as well, the plain segment-fastest order measured 1-3% faster than
-// a row block's segments on one XCD, with 512- and with 256-column tiles.
+// a row block's segments on one XCD, with 512- and with 256-column tiles, and
+// 2-11% faster than units of 8, 32 or 128 row bands per XCD.
 template <bool kRow, bool kFQRow>
 constexpr bool kColTUnits = !kRow && !kFQRow;
 
