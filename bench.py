@@ -30,9 +30,10 @@ Besides the timed steps it reports, in the same line:
   ceilings      per read:write mix (read, write, copy, row-wise quantize,
                 one-pass, dequantize, FP4 encode, FP4 dequantize, FP8 block to
                 MXFP8), the best rate of several trivial-arithmetic streaming
-                patterns (bench_streams.hip: the quantizers' tiles in the plain
-                and the XCD row-block order, and grid-stride walks) over cold
-                inputs; ceiling_runs lists every pattern's rate
+                patterns (bench_streams.hip: the quantizers' 512-column tiles
+                and half-width 256-column ones, in the plain and the XCD
+                row-block order, and grid-stride walks) over cold inputs;
+                ceiling_runs lists every pattern's rate
   cpu_baseline  the CPU oracle (single-threaded C) timed on a bounded sample
                 of the same workload, and the same sharded over host threads
   breakdown     every other quantizer workload (row-wise weight, grouped MoE
@@ -183,8 +184,8 @@ def warm_up(launch, arg_sets, min_launches=16):
 
 
 def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20, mixes=None):
-    """Best GB/s per mix over the tiled (R = 1, 2, 4, 8 rows per wave; plain or
-    XCD row-block order) and flat
+    """Best GB/s per mix over the tiled (512- or 256-column tiles; R = 1, 2,
+    4, 8 rows per wave; plain or XCD row-block order) and flat
     (U = 2, 4, 8 vectors in flight; 1024, 2048, 4096 workgroups) patterns,
     each timed like the quantizers: back-to-back launches cycling over cold
     inputs after an untimed warm-up.  The mixes that read x cycle over the
@@ -223,9 +224,10 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20, mixes=None):
         return a.elapsed_time(b) / iters * 1e-3
 
     runs = {}
-    for v in range(8 * len(MIXES)):
+    for v in range(16 * len(MIXES)):
         mix, R = MIXES[(v // 4) % len(MIXES)], 1 << (v % 4)
-        order = " xcd" if v >= 4 * len(MIXES) else ""
+        order = " xcd" if (v // (4 * len(MIXES))) % 2 else ""
+        order += " 256c" if v >= 8 * len(MIXES) else ""
         if mixes is not None and mix not in mixes:
             continue
 

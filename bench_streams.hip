@@ -10,7 +10,9 @@
 //          plain segment-fastest order or the quantizers' XCD order, per lane and
 //          row the mix's bytes: 16 bytes of bf16 or 8 (4) bytes of codes read,
 //          8 / 16 / 4 bytes written per plane, and one byte per lane quad and
-//          row (a scale byte per 32 elements) where the mix has scales;
+//          row (a scale byte per 32 elements) where the mix has scales; and
+//          the same with half-width lanes: 256-column tiles, 4 elements per
+//          lane (8 bytes of bf16), a scale byte per lane octet;
 //   flat   a grid-stride walk over the tensor as one array, U vectors in
 //          flight per lane, the same bytes per element without scales.
 // Read-only kernels fold what they load into a word that is stored only if it
@@ -112,6 +114,65 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t *__restrict__
     if (!M::writes && fold == kNever) sink[0] = fold;
 }
 
+// The tiled pattern with half-width lanes: 256-column tiles, 4 elements per
+// lane and row (8 bytes of bf16, 4 of 8-bit codes, 2 of 4-bit codes read;
+// 4 / 8 / 2 bytes written per plane).
+template <int R, int K, bool X>
+__global__ __launch_bounds__(256) void half_kernel(const uint16_t *__restrict__ x, int64_t rows,
+                                                  int64_t cols, int64_t nseg,
+                                                  uint8_t *__restrict__ o8a,
+                                                  uint8_t *__restrict__ o8b,
+                                                  uint16_t *__restrict__ o16,
+                                                  uint8_t *__restrict__ sc,
+                                                  uint32_t *__restrict__ sink)
+{
+    using M = Mix<K>;
+    int64_t seg, rb;
+    if (X) {
+        if (!mxq::xcd_row_tile(nseg, (rows + 4 * R - 1) / (4 * R), seg, rb)) return;
+    } else {
+        seg = blockIdx.x % nseg;
+        rb = blockIdx.x / nseg;
+    }
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t col = seg * 256 + lane * 4;
+    const int64_t r0 = rb * (4 * R) + wave;
+    uint2 v[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t r = r0 + 4 * i;
+        v[i] = make_uint2((uint32_t)r, (uint32_t)col);
+        if (r >= rows) continue;
+        if (M::rd == 16) {
+            v[i] = ld8<true>(x + r * cols + col);
+        } else if (M::rd == 8) {
+            const uint32_t c = ld4<false>(o8a + r * cols + col);
+            v[i] = make_uint2(c, c ^ 1u);
+        } else if (M::rd == 4) {
+            const uint32_t c = *reinterpret_cast<const uint16_t *>(o8a + r * (cols >> 1) + (col >> 1));
+            v[i] = make_uint2(c, c ^ 2u);
+        }
+        if (M::sc_rd) v[i].y ^= sc[r * (cols >> 5) + (col >> 5)];
+    }
+    uint32_t fold = 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t r = r0 + 4 * i;
+        if (r >= rows) continue;
+        const uint32_t c = __builtin_amdgcn_perm(v[i].y, v[i].x, 0x06040200u);
+        if (M::w8 > 0) st4<true>(o8a + r * cols + col, c);
+        if (M::w8 > 1) st4<true>(o8b + r * cols + col, c ^ 0x01010101u);
+        if (M::w16 > 0) st8<true>(o16 + r * cols + col, v[i]);
+        if (M::w4 > 0)
+            *reinterpret_cast<uint16_t *>(o8b + r * (cols >> 1) + (col >> 1)) = (uint16_t)(c ^ (c >> 16));
+        if (M::w8b > 0) st4<true>(o8b + r * cols + col, c);
+        if (M::sc_wr) sc[r * (cols >> 5) + (col >> 5)] = (uint8_t)c;
+        fold ^= v[i].x ^ v[i].y;
+    }
+    if (!M::writes && fold == kNever) sink[0] = fold;
+}
+
 // One element group per 16 bytes of bf16 (8 elements): x as nvec 16-byte
 // vectors; codes o8a as nvec 8-byte vectors (4-byte for the FP4 mixes); o8b
 // nvec 8-byte vectors; o16 nvec 16-byte vectors.
@@ -171,19 +232,23 @@ const char *bench_streams_build_id(void) { return STREAMS_BUILD_ID; }
 int bench_streams_kinds(void) { return kKinds; }
 
 // Tiled variants: variant = R index (0: R=1, 1: R=2, 2: R=4, 3: R=8) + 4 * kind
-// + 4 * kinds * order (0: segment-fastest, 1: a row block's segments on one XCD).
-// x [rows, cols] bf16 with cols % 512 == 0; o8a, o8b [rows, cols] bytes (the
-// codes the 8- and 4-byte reading kinds read are o8a); o16 [rows, cols] bf16;
-// sc [rows, cols/32] bytes; sink one word.  Returns 0, 1 for a bad argument
-// (nothing launched), 2 for a launch error.
+// + 4 * kinds * order (0: segment-fastest, 1: a row block's segments on one XCD)
+// + 8 * kinds * width (0: 512-column tiles, 16 bytes of bf16 per lane; 1:
+// 256-column tiles, 8 bytes).  x [rows, cols] bf16 with cols a multiple of the
+// tile width; o8a, o8b [rows, cols] bytes (the codes the 8- and 4-byte reading
+// kinds read are o8a); o16 [rows, cols] bf16; sc [rows, cols/32] bytes; sink
+// one word.  Returns 0, 1 for a bad argument (nothing launched), 2 for a
+// launch error.
 int bench_stream_tiled(int variant, const void *x, int64_t rows, int64_t cols, void *o8a,
                        void *o8b, void *o16, void *sc, void *sink, void *stream)
 {
-    if (variant < 0 || variant >= 8 * kKinds || rows <= 0 || cols <= 0 || cols % 512 != 0)
-        return 1;
+    if (variant < 0 || variant >= 16 * kKinds || rows <= 0 || cols <= 0) return 1;
+    const bool half = variant >= 8 * kKinds;
+    const int64_t tw = half ? 256 : 512;
+    if (cols % tw != 0) return 1;
     if (!x || !o8a || !o8b || !o16 || !sc || !sink) return 1;
-    const int64_t nseg = cols / 512;
-    const int ri = variant % 4, kind = (variant / 4) % kKinds, xcd = variant / (4 * kKinds);
+    const int64_t nseg = cols / tw;
+    const int ri = variant % 4, kind = (variant / 4) % kKinds, xcd = (variant / (4 * kKinds)) & 1;
     const int R = 1 << ri;
     const int64_t nrb = (rows + 4 * R - 1) / (4 * R);
     const int64_t tiles = xcd ? mxq::xcd_row_grid(nseg, nrb) : nseg * nrb;
@@ -195,7 +260,13 @@ int bench_stream_tiled(int variant, const void *x, int64_t rows, int64_t cols, v
     uint32_t *k = (uint32_t *)sink;
 #define TL(RR, KK)                                                                                 \
     do {                                                                                           \
-        if (xcd)                                                                                   \
+        if (half && xcd)                                                                           \
+            hipLaunchKernelGGL((half_kernel<RR, KK, true>), dim3((unsigned)tiles), dim3(256), 0,  \
+                               s, xp, rows, cols, nseg, a, b, f, c, k);                            \
+        else if (half)                                                                             \
+            hipLaunchKernelGGL((half_kernel<RR, KK, false>), dim3((unsigned)tiles), dim3(256), 0, \
+                               s, xp, rows, cols, nseg, a, b, f, c, k);                            \
+        else if (xcd)                                                                              \
             hipLaunchKernelGGL((tiled_kernel<RR, KK, true>), dim3((unsigned)tiles), dim3(256), 0, \
                                s, xp, rows, cols, nseg, a, b, f, c, k);                            \
         else                                                                                       \
