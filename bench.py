@@ -616,6 +616,14 @@ def main():
             [lambda: check(lib.nvfp4_quantize_grouped(nvd, len(gu), P(nvg), n_exp, P(nvw), nvw_n,
                                                       sp), "nvfp4 grouped")],
             2 * gue + gue // 2 + gue // 16 + 4 * n_exp, iters=10)
+        # its amax pass reads every tensor (the read-only mix), its encoding
+        # pass reads them again and writes codes and scales (the FP4-encode
+        # mix): the two act_16384 streams back to back bound the pair
+        r = breakdown["moe gate/up NVFP4 grouped, shared scale per expert (unique bytes)"]
+        two = (2 * gue / ceilings["read"]["GB/s"] + (2 * gue + gue // 2 + gue // 16)
+               / ceilings["fp4"]["GB/s"]) / 1e3
+        r["two_stream_us"] = round(two, 2)
+        r["frac_two_stream"] = round(two / r["us"], 4)
         del xs, nv_outs, nvw
         torch.cuda.empty_cache()
 
