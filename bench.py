@@ -62,6 +62,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 BATCHES = 4            # resident batches the main step loop cycles through
 COLD_INPUT_BYTES = 1e9  # other workloads: input bytes read between two reads of one copy
 MAX_COPIES = 32
+QT_PAD = 256  # bytes between the transposed codes' rows beyond `rows`, for the padded entry
 METRIC = "MXFP8 quantize GB/s (bf16 in + fp8/scale out) and % of HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "block_scaled_precision_mxfp8_amd", "csrc", f)
@@ -311,7 +312,8 @@ def main():
                 "qr": torch.empty((rows, cols), dtype=torch.uint8, device=dev),
                 "sr": torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
                 "fq": torch.empty((rows, cols), dtype=torch.bfloat16, device=dev),
-                "qt": torch.empty((cols, rows), dtype=torch.uint8, device=dev),
+                # room for qT rows padded by QT_PAD bytes (the padded entry)
+                "qt": torch.empty((cols * (rows + QT_PAD),), dtype=torch.uint8, device=dev),
                 "st": torch.empty((cols, (rows + 31) // 32), dtype=torch.uint8, device=dev),
                 "S1": torch.empty((rows, cols // 128), dtype=torch.float32, device=dev),
                 "q4": torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
@@ -504,6 +506,14 @@ def main():
             [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]), rows,
                                                           P(d["st"]), P(d["qr"]), P(d["sr"]),
                                                           P(d["fq"]), sp), "colwise_t")
+             for d in batches], step_bytes, mix="onepass")
+        # the same with qT rows QT_PAD bytes apart instead of `rows`: row
+        # strides of a multiple of 4 KiB put the workgroups' concurrent
+        # 128-byte column pieces on a subset of the memory channels
+        breakdown[f"act_16384 one-pass, column-wise transposed, qT rows padded by {QT_PAD} B"] = rotated(
+            [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]),
+                                                          rows + QT_PAD, P(d["st"]), P(d["qr"]),
+                                                          P(d["sr"]), P(d["fq"]), sp), "colwise_t")
              for d in batches], step_bytes, mix="onepass")
         breakdown["act_16384 column-wise transposed only"] = rotated(
             [lambda d=d: check(lib.mxq_quantize_colwise_t(P(d["x"]), rows, cols, P(d["qt"]), rows,

@@ -14,10 +14,10 @@ from gpu_util import announce, assert_same, bits16, to_dev_bf16, u8
 pytestmark = pytest.mark.gpu
 
 
-def check_colwise_t(gpu, orc, x_bits, name, rowwise=True, fake_quant=True):
-    announce(f"colwise_t {name} {x_bits.shape} row={rowwise} fq={fake_quant}")
+def check_colwise_t(gpu, orc, x_bits, name, rowwise=True, fake_quant=True, ldt=None):
+    announce(f"colwise_t {name} {x_bits.shape} row={rowwise} fq={fake_quant} ldt={ldt}")
     x = to_dev_bf16(x_bits)
-    out = gpu.quantize_colwise_t(x, rowwise=rowwise, fake_quant=fake_quant)
+    out = gpu.quantize_colwise_t(x, rowwise=rowwise, fake_quant=fake_quant, ldt=ldt)
     torch.cuda.synchronize()
     oqt, ost = orc.mxfp8_quantize_colwise_t(x_bits)
     assert_same(f"{name} qt", u8(out["q_colT"]), oqt)
@@ -35,6 +35,15 @@ def check_colwise_t(gpu, orc, x_bits, name, rowwise=True, fake_quant=True):
                                    (4097, 544), (160, 7168), (256, 1024)])
 def test_colwise_t_shapes(gpu, orc, shape):
     check_colwise_t(gpu, orc, workloads.random_bf16(shape, 31 * shape[0] + shape[1]), f"t{shape}")
+
+
+@pytest.mark.parametrize("shape,pad", [((4096, 1024), 256), ((300, 544), 16), ((129, 7168), 4096)])
+def test_colwise_t_padded_rows(gpu, orc, shape, pad):
+    """q_colT rows spaced ldt = rows (rounded up to 16) + pad bytes apart: the
+    view holds the same codes as the oracle's compact layout."""
+    ldt = (shape[0] + 15) // 16 * 16 + pad
+    check_colwise_t(gpu, orc, workloads.random_bf16(shape, shape[0] * 3 + pad), f"t-pad{pad}{shape}",
+                    ldt=ldt)
 
 
 @pytest.mark.parametrize("rowwise,fake_quant", [(False, False), (True, False), (False, True)])
@@ -101,3 +110,10 @@ def test_colwise_t_guard_bands(gpu, orc):
     assert_same("guard qt", qm[:, :rows], oqt)
     assert np.all(qm[:, rows:] == 0xA5)
     assert_same("guard st", sh[G:G + cols * nrg].reshape(cols, nrg), ost)
+
+
+def test_colwise_t_binding_refuses_bad_ldt(gpu):
+    x = to_dev_bf16(workloads.random_bf16((64, 96), 5))
+    for ldt in (48, 72):  # below rows; not a multiple of 16
+        with pytest.raises(ValueError):
+            gpu.quantize_colwise_t(x, ldt=ldt)
