@@ -634,6 +634,7 @@ def main():
                / ceilings["fp4"]["GB/s"]) / 1e3
         r["two_stream_us"] = round(two, 2)
         r["frac_two_stream"] = round(two / r["us"], 4)
+        r["two_stream_on"] = "act_16384 batches"
         del xs, nv_outs, nvw
         torch.cuda.empty_cache()
 
@@ -712,6 +713,7 @@ def main():
                / sq_ceilings["fp4"]["GB/s"]) / 1e3
         r["two_stream_us"] = round(two, 2)
         r["frac_two_stream"] = round(two / r["us"], 4)
+        r["two_stream_on"] = "square_8192 buffers"
         del ysets, sq_batches
 
     out = {
