@@ -317,7 +317,6 @@ __device__ __forceinline__ void mx_colsplit_body(
     uint4 *__restrict__ part)
 {
     constexpr int kRW = 32 / kW;  // rows per wave
-    constexpr bool kRowAny = kRow || kFQRow;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const bool cin = kFull || col < cols;
@@ -392,27 +391,29 @@ __device__ __forceinline__ void mx_colsplit_body(
                                           bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16)));
         }
     };
-    auto row_work = [&](int i) __attribute__((always_inline)) {
+    auto row_codes = [&](int i) __attribute__((always_inline)) {
+        const int64_t r = r0 + kW * i;
+        const bool ok = kFull || (cin && r < rows);
+        const MxRow8 m = mx_row_encode8(v[i]);
+        if (ok) {
+            st8<kNTStore>(qr + r * cols + col, make_uint2(m.c0, m.c1));
+            sr[r * ngr + (col >> 5)] = (uint8_t)m.s;  // same byte from the 4 lanes of a quad
+        }
+    };
+    auto row_fake_quant = [&](int i) __attribute__((always_inline)) {
         const int64_t r = r0 + kW * i;
         const bool ok = kFull || (cin && r < rows);
         const MxRow8 m = mx_row_encode8(v[i]);
         const bool nan_group = m.s == 0xFFu;
-        if (kRow && ok) {
-            st8<kNTStore>(qr + r * cols + col, make_uint2(m.c0, m.c1));
-            sr[r * ngr + (col >> 5)] = (uint8_t)m.s;  // same byte from the 4 lanes of a quad
+        uint2 lo, hi;
+        if (wave_any(nan_group)) {
+            lo = mx_dequant4(m.c0, (int)m.s - 7, nan_group);
+            hi = mx_dequant4(m.c1, (int)m.s - 7, nan_group);
+        } else {
+            lo = mx_dequant4_hw(m.c0, m.sf);
+            hi = mx_dequant4_hw(m.c1, m.sf);
         }
-        if (kFQRow) {
-            uint2 lo, hi;
-            if (wave_any(nan_group)) {
-                lo = mx_dequant4(m.c0, (int)m.s - 7, nan_group);
-                hi = mx_dequant4(m.c1, (int)m.s - 7, nan_group);
-            } else {
-                lo = mx_dequant4_hw(m.c0, m.sf);
-                hi = mx_dequant4_hw(m.c1, m.sf);
-            }
-            if (ok)
-                st16<kNTStore>(fq_row + r * cols + col, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        }
+        if (ok) st16<kNTStore>(fq_row + r * cols + col, make_uint4(lo.x, lo.y, hi.x, hi.y));
     };
     static_for<0, kRW, 2>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
@@ -440,9 +441,20 @@ __device__ __forceinline__ void mx_colsplit_body(
         put_col_row(i, a0, a1);
         put_col_row(i + 1, b0, b1);
     });
-    if (kRowAny) {
+    // then the row-wise codes and scales of all the wave's rows, then their
+    // fake-quant rows, each row encoded again from x (still in registers).
+    // On the one pass this measured 0.8% faster than writing each row's
+    // codes and fake-quant together (118.7 against 119.6 us, mean of 15
+    // paired rounds); keeping the codes in registers between the two loops
+    // instead measured 0.4% slower than writing them together.
+    if (kRow) {
         static_for<0, kRW, 1>([&](auto ic) __attribute__((always_inline)) {
-            row_work(decltype(ic)::value);
+            row_codes(decltype(ic)::value);
+        });
+    }
+    if (kFQRow) {
+        static_for<0, kRW, 1>([&](auto ic) __attribute__((always_inline)) {
+            row_fake_quant(decltype(ic)::value);
         });
     }
 }
