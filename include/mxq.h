@@ -134,6 +134,10 @@ mxq_status mxq_quantize_colwise(const uint16_t *x, int64_t rows, int64_t cols,
  *       (qr and sr together or neither; fq alone is allowed)
  * x [rows, cols] bf16 contiguous, 16-byte aligned.  Shape: cols % 32 == 0;
  * any rows >= 0.  Bytes of qt between rows and ldt are not written.
+ * Performance: with the row-wise outputs requested and ldt a multiple of
+ * 4096, every row of qt starts on the same 4 KiB boundary; on MI355X a stride
+ * of ldt + 256 measured about 4% faster for that call (the compact stride is
+ * the faster one for the column-only call).
  */
 mxq_status mxq_quantize_colwise_t(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qt,
                                   int64_t ldt, uint8_t *st, uint8_t *qr, uint8_t *sr,
