@@ -186,7 +186,8 @@ def warm_up(launch, arg_sets, min_launches=16):
 
 def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20, mixes=None):
     """Best GB/s per mix over the tiled (512- or 256-column tiles; R = 1, 2,
-    4, 8 rows per wave; plain or XCD row-block order) and flat
+    4, 8 rows per wave; plain or XCD row-block order; up to 8 or at most 5
+    resident workgroups per CU) and flat
     (U = 2, 4, 8 vectors in flight; 1024, 2048, 4096 workgroups) patterns,
     each timed like the quantizers: back-to-back launches cycling over cold
     inputs after an untimed warm-up.  The mixes that read x cycle over the
@@ -225,10 +226,11 @@ def measure_ceilings(L, batches, rows, cols, stream, sp, iters=20, mixes=None):
         return a.elapsed_time(b) / iters * 1e-3
 
     runs = {}
-    for v in range(16 * len(MIXES)):
+    for v in range(32 * len(MIXES)):
         mix, R = MIXES[(v // 4) % len(MIXES)], 1 << (v % 4)
         order = " xcd" if (v // (4 * len(MIXES))) % 2 else ""
-        order += " 256c" if v >= 8 * len(MIXES) else ""
+        order += " 256c" if (v // (8 * len(MIXES))) % 2 else ""
+        order += " cap5" if v >= 16 * len(MIXES) else ""
         if mixes is not None and mix not in mixes:
             continue
 

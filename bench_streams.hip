@@ -234,7 +234,9 @@ int bench_streams_kinds(void) { return kKinds; }
 // Tiled variants: variant = R index (0: R=1, 1: R=2, 2: R=4, 3: R=8) + 4 * kind
 // + 4 * kinds * order (0: segment-fastest, 1: a row block's segments on one XCD)
 // + 8 * kinds * width (0: 512-column tiles, 16 bytes of bf16 per lane; 1:
-// 256-column tiles, 8 bytes).  x [rows, cols] bf16 with cols a multiple of the
+// 256-column tiles, 8 bytes) + 16 * kinds * cap (1: 27 KiB of unused dynamic
+// LDS per workgroup, so at most 5 workgroups reside on a CU, as the row-wise
+// quantizers launch).  x [rows, cols] bf16 with cols a multiple of the
 // tile width; o8a, o8b [rows, cols] bytes (the codes the 8- and 4-byte reading
 // kinds read are o8a); o16 [rows, cols] bf16; sc [rows, cols/32] bytes; sink
 // one word.  Returns 0, 1 for a bad argument (nothing launched), 2 for a
@@ -242,8 +244,9 @@ int bench_streams_kinds(void) { return kKinds; }
 int bench_stream_tiled(int variant, const void *x, int64_t rows, int64_t cols, void *o8a,
                        void *o8b, void *o16, void *sc, void *sink, void *stream)
 {
-    if (variant < 0 || variant >= 16 * kKinds || rows <= 0 || cols <= 0) return 1;
-    const bool half = variant >= 8 * kKinds;
+    if (variant < 0 || variant >= 32 * kKinds || rows <= 0 || cols <= 0) return 1;
+    const bool half = (variant / (8 * kKinds)) % 2 == 1;
+    const size_t dyn = variant >= 16 * kKinds ? 27 * 1024 : 0;
     const int64_t tw = half ? 256 : 512;
     if (cols % tw != 0) return 1;
     if (!x || !o8a || !o8b || !o16 || !sc || !sink) return 1;
@@ -261,16 +264,16 @@ int bench_stream_tiled(int variant, const void *x, int64_t rows, int64_t cols, v
 #define TL(RR, KK)                                                                                 \
     do {                                                                                           \
         if (half && xcd)                                                                           \
-            hipLaunchKernelGGL((half_kernel<RR, KK, true>), dim3((unsigned)tiles), dim3(256), 0,  \
+            hipLaunchKernelGGL((half_kernel<RR, KK, true>), dim3((unsigned)tiles), dim3(256), dyn, \
                                s, xp, rows, cols, nseg, a, b, f, c, k);                            \
         else if (half)                                                                             \
-            hipLaunchKernelGGL((half_kernel<RR, KK, false>), dim3((unsigned)tiles), dim3(256), 0, \
+            hipLaunchKernelGGL((half_kernel<RR, KK, false>), dim3((unsigned)tiles), dim3(256), dyn, \
                                s, xp, rows, cols, nseg, a, b, f, c, k);                            \
         else if (xcd)                                                                              \
-            hipLaunchKernelGGL((tiled_kernel<RR, KK, true>), dim3((unsigned)tiles), dim3(256), 0, \
+            hipLaunchKernelGGL((tiled_kernel<RR, KK, true>), dim3((unsigned)tiles), dim3(256), dyn, \
                                s, xp, rows, cols, nseg, a, b, f, c, k);                            \
         else                                                                                       \
-            hipLaunchKernelGGL((tiled_kernel<RR, KK, false>), dim3((unsigned)tiles), dim3(256), 0,\
+            hipLaunchKernelGGL((tiled_kernel<RR, KK, false>), dim3((unsigned)tiles), dim3(256), dyn,\
                                s, xp, rows, cols, nseg, a, b, f, c, k);                            \
     } while (0)
 #define TL_KIND(RR)                                                                                \

@@ -41,6 +41,18 @@ constexpr int rows_row_tile(bool q, bool fq) { return (q && !fq) ? kRowsRowQ : k
 // were 3% (row groups) and 7% (column groups) faster, and 8 rows another 1%
 // and 1.5%.
 constexpr int kRowsDq = 8;
+// Resident-workgroup cap for the single-output row-wise launches (codes and
+// scales only, or fake-quant only) and the grouped launch.  Their 4-wave
+// workgroups need few VGPRs (27-52), so 8 fit on a CU; each launch reserves
+// 27 KiB of dynamic LDS that no kernel touches, which leaves room for 5 in a
+// CU's 160 KiB.  MI355X, inputs cold in HBM, variants interleaved in one
+// process, medians of 5 rounds: row-wise quantize of [16384, 7168]
+// 55.5 -> 54.3 us, fake-quant only 72.5 -> 70.9 us, the grouped launch over
+// the 384 MoE tensors 2747 -> 2717 us; 6 resident measured close behind, 4
+// and 3 slower.  The column-wise launches hold 4 (by VGPRs) and ran slower
+// with fewer; the same cap slowed the 1 x 128 block-FP8 quantizer (12%) and
+// the column-group dequantizer (5%), which keep 0.
+constexpr size_t kLdsCap5 = 27 * 1024;
 constexpr int kColTileRows = 128;  // rows per transposed column-wise workgroup tile (4 waves x 32)
 // Streaming (non-temporal) hints on every load and store: each byte is
 // touched once.  Measured on MI355X with the [16384, 7168] activation read
@@ -761,11 +773,11 @@ hipError_t launch_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int6
         hipLaunchKernelGGL((mx_rowwise_kernel<true, true>), grid, block, 0, stream, x, rows, cols,
                            ldx, q, ldq, scale, lds, fq, ldf, nseg);
     else if (q)
-        hipLaunchKernelGGL((mx_rowwise_kernel<true, false>), grid, block, 0, stream, x, rows, cols,
-                           ldx, q, ldq, scale, lds, fq, ldf, nseg);
+        hipLaunchKernelGGL((mx_rowwise_kernel<true, false>), grid, block, kLdsCap5, stream, x,
+                           rows, cols, ldx, q, ldq, scale, lds, fq, ldf, nseg);
     else
-        hipLaunchKernelGGL((mx_rowwise_kernel<false, true>), grid, block, 0, stream, x, rows, cols,
-                           ldx, q, ldq, scale, lds, fq, ldf, nseg);
+        hipLaunchKernelGGL((mx_rowwise_kernel<false, true>), grid, block, kLdsCap5, stream, x,
+                           rows, cols, ldx, q, ldq, scale, lds, fq, ldf, nseg);
     return hipGetLastError();
 }
 
@@ -860,8 +872,8 @@ hipError_t launch_mx_grouped(const GroupEntry *table_dev, const int32_t *starts_
 {
     if (n <= 0 || total_tiles <= 0) return hipSuccess;
     if (total_tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)total_tiles), dim3(256), 0, stream,
-                       table_dev, starts_dev, n);
+    hipLaunchKernelGGL(mx_grouped_kernel, dim3((unsigned)total_tiles), dim3(256), kLdsCap5,
+                       stream, table_dev, starts_dev, n);
     return hipGetLastError();
 }
 

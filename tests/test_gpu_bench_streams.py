@@ -45,7 +45,7 @@ def test_every_tiled_variant_stays_in_its_buffers(streams, sp):
     kinds = streams.bench_streams_kinds()
     assert kinds == len(bench.MIXES)
     sizes = {"x": 2 * E, "o8a": E, "o8b": E, "o16": 2 * E, "sc": E // 32}
-    for v in range(16 * kinds):  # 4 tile heights x kinds x 2 workgroup orders x 2 tile widths
+    for v in range(32 * kinds):  # 4 tile heights x kinds x 2 orders x 2 tile widths x 2 caps
         announce(f"bench_stream_tiled variant {v}")
         b = {k: _buf(n) for k, n in sizes.items()}
         sink = _buf(64)
@@ -82,7 +82,7 @@ def test_bad_arguments_are_refused_before_any_launch(streams, sp):
     sink = _buf(64)
     before = b.clone()
     null = ctypes.c_void_p(None)
-    for v, rows, cols, o8a in ((-1, ROWS, COLS, b), (16 * kinds, ROWS, COLS, b),
+    for v, rows, cols, o8a in ((-1, ROWS, COLS, b), (32 * kinds, ROWS, COLS, b),
                                (0, ROWS, 1000, b), (0, ROWS, 768, b), (8 * kinds, ROWS, 1000, b),
                                (0, 0, COLS, b), (0, ROWS, COLS, None)):
         st = streams.bench_stream_tiled(v, _p(b), rows, cols, null if o8a is None else _p(b),
