@@ -50,6 +50,16 @@ static_assert(kBlk % kRowsDq == 0 && kBlk % kRowsBq == 0,
 // encoding pass; the grouped amax pass streams (its tensors together far
 // exceed that cache: 2.87 -> 2.72 ms on 256 MoE gate/up tensors).
 constexpr bool kNTStore = true;
+// Resident-workgroup cap for the single-tensor NVFP4 launches (amax pass,
+// encoding pass, dequantize): 23 KiB of dynamic LDS that no kernel touches
+// leaves room for 6 of their 4-wave workgroups in a CU's 160 KiB instead of
+// the 8 their VGPRs allow.  MI355X, [8192, 8192] cold in HBM, variants
+// interleaved in one process, medians of 6 rounds: quantize (three launches)
+// 49.99 -> 49.16 us, dequantize 30.12 -> 29.25 us; 5 resident measured the
+// same for quantize and 1% slower for dequantize.  The grouped NVFP4 passes
+// ran 10% slower under such a cap and the block-FP8 quantizers and
+// dequantizer slower or no faster; they keep 0.
+constexpr size_t kLdsCap6 = 23 * 1024;
 constexpr bool kNTLoad = true;
 constexpr bool kNTLoadDq = false;
 constexpr bool kNTLoadRequant = true;
@@ -805,15 +815,16 @@ hipError_t launch_nvfp4_quant(const uint16_t *x, int64_t rows, int64_t cols, uin
     const int64_t nseg = (cols + kSegNv - 1) / kSegNv;
     const int64_t tiles = xcd_row_grid(nseg, (rows + kRowsNvQ - 1) / kRowsNvQ);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream, x, nvec, ws);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), kLdsCap6, stream, x,
+                       nvec, ws);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(nvfp4_finalize_kernel, dim3(1), dim3(kNvAmaxBlocks), 0, stream, ws, ablocks,
                        g);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, x, rows,
-                       cols, q, s, g, nseg);
+    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)tiles), dim3(256), kLdsCap6, stream, x,
+                       rows, cols, q, s, g, nseg);
     return hipGetLastError();
 }
 
@@ -909,8 +920,8 @@ hipError_t launch_nvfp4_dequant(const uint8_t *q, const uint8_t *s, const float 
     if (nseg <= 0 || nrb <= 0) return hipSuccess;
     const int64_t tiles = xcd_row_grid(nseg, nrb);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, q, s, g,
-                       rows, cols, out, nseg);
+    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3((unsigned)tiles), dim3(256), kLdsCap6, stream, q,
+                       s, g, rows, cols, out, nseg);
     return hipGetLastError();
 }
 
